@@ -1,0 +1,7 @@
+"""fp64 CPU oracle for exact attention: test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from this package.  The HIP library and its
+Python binding never do, and this package imports nothing from them.
+"""
+from .ref import ref_bwd, ref_bwd_delta, ref_fwd, ref_probs  # noqa: F401
