@@ -1,0 +1,86 @@
+// fa_api.cpp - extern "C" entry points of libfa.so (declared in include/fa.h).
+// Validates every argument before anything is enqueued, checks that the
+// current device is a gfx950, and launches the kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_validate.h"
+
+namespace fa {
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                           int d, float scale, int causal, hipStream_t st);
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+                          int N, int d, float scale, int causal, hipStream_t st);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                      int causal, void* ws, hipStream_t st);
+
+namespace {
+// Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, 2 no.  Written
+// once per device; a benign cache of an immutable device property.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kErrDevice;
+  if (dev < kMaxDevices) {
+    const int known = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (known == 1) return kOk;
+    if (known == 2) return kErrDevice;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return kErrDevice;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? kOk : kErrDevice;
+}
+}  // namespace
+}  // namespace fa
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_fwd(q, k, v, o, lse, s, scale, causal, 2);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, causal, stream) == hipSuccess ? fa::kOk
+                                                                                               : fa::kErrHip;
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_fwd(q, k, v, o, lse, s, scale, causal, 4);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream) == hipSuccess ? fa::kOk
+                                                                                              : fa::kErrHip;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) { return fa::bwd_workspace_bytes(fa::Shape{B, H, N, d}); }
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+           void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, workspace, workspace_bytes);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, workspace, stream) ==
+                 hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+const char* fa_status_string(int status) { return fa::status_string(status); }
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// fa_common.h - device-side types and helpers shared by the gfx950 kernels.
+#ifndef FA_COMMON_H_
+#define FA_COMMON_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// v_mfma_f32_32x32x16_bf16.  Lane l supplies row (l % 32) of A and column
+// (l % 32) of B, each with eight k-values; lanes l and l+32 together cover
+// the 16 k-values, with the same k assignment for A and B, so any fixed
+// bijection between (l / 32, element) and k gives A*B.  The accumulator
+// element j of lane l is C[8*(j/4) + 4*(l/32) + j%4][l % 32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row index (within a 32x32 accumulator block) held by element j of lane l.
+__device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_swap32(float x) { return __shfl_xor(x, 32); }
+
+// XOR swizzle of 16-byte units within an LDS row, chosen so that 16
+// consecutive rows read at the same logical unit hit 16 distinct 16-byte bank
+// groups (and 8 consecutive rows hit 8 distinct groups of a 128-byte window).
+//   rows of 16 units (256 B): unit ^ (row % 16)
+//   rows of  8 units (128 B): unit ^ ((row ^ row/8) % 8)
+template <int UNITS>
+__device__ __forceinline__ int swz(int row, int unit) {
+  if constexpr (UNITS == 16) return unit ^ (row & 15);
+  else return unit ^ ((row ^ (row >> 3)) & 7);
+}
+
+// Pack two fp32 values into two bf16 (round to nearest even) in one dword.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  unsigned short ua = __builtin_bit_cast(unsigned short, a);
+  unsigned short ub = __builtin_bit_cast(unsigned short, b);
+  return unsigned(ua) | (unsigned(ub) << 16);
+}
+
+// Map a linear workgroup id to a tile id so that the tiles of one (b, h)
+// head are contiguous within one XCD: workgroups are handed to the 8 XCDs
+// round-robin, so id w runs on XCD w % 8.  When the grid is not a multiple of
+// 8 the identity is used.
+__device__ __forceinline__ int xcd_remap(int w, int G) {
+  if ((G & 7) != 0) return w;
+  return (w & 7) * (G >> 3) + (w >> 3);
+}
+
+}  // namespace fa
+
+#endif  // FA_COMMON_H_

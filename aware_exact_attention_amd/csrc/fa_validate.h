@@ -1,0 +1,120 @@
+// fa_validate.h - argument checks of the C ABI, pure C++ (no HIP), so that the
+// same code is unit-tested on a CPU-only host with g++ and used by libfa.so.
+// Every check runs before anything is enqueued; the first failing check
+// decides the status.
+#ifndef FA_VALIDATE_H_
+#define FA_VALIDATE_H_
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+namespace fa {
+
+// Status values mirror fa_status in include/fa.h.
+enum : int {
+  kOk = 0, kErrNull = -1, kErrShape = -2, kErrHeadDim = -3, kErrScale = -4,
+  kErrAlign = -5, kErrWorkspace = -6, kErrDevice = -7, kErrHip = -8, kErrArg = -9
+};
+
+struct Shape {
+  int B, H, N, d;
+};
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Elements per [B][H][N][d] tensor, or -1 if the shape is invalid / too large.
+inline int64_t tensor_elems(const Shape& s) {
+  if (s.B < 1 || s.H < 1 || s.N < 1 || s.d < 1) return -1;
+  const int64_t n = int64_t(s.B) * s.H * s.N * s.d;
+  if (n >= (int64_t(1) << 31)) return -1;
+  return n;
+}
+
+inline int check_common(const Shape& s, float scale, int causal) {
+  if (tensor_elems(s) < 0) return kErrShape;
+  if (s.d != 64 && s.d != 128) return kErrHeadDim;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return kErrScale;
+  if (causal != 0 && causal != 1) return kErrArg;
+  return kOk;
+}
+
+// Byte ranges [p, p+n) overlap?
+inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Forward: inputs q,k,v (elem_bytes each element), outputs o (same), lse (float per row).
+inline int validate_fwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                        const Shape& s, float scale, int causal, size_t elem_bytes) {
+  if (!q || !k || !v || !o || !lse) return kErrNull;
+  int st = check_common(s, scale, causal);
+  if (st != kOk) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return kErrAlign;
+  const size_t tb = size_t(tensor_elems(s)) * elem_bytes;
+  const size_t lb = size_t(s.B) * s.H * s.N * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins) {
+    if (overlaps(in, tb, o, tb) || overlaps(in, tb, lse, lb)) return kErrArg;
+  }
+  if (overlaps(o, tb, lse, lb)) return kErrArg;
+  return kOk;
+}
+
+// Workspace of the backward: fp32 dQ accumulator, then fp32 D row terms,
+// each rounded up to 256 bytes.
+inline size_t bwd_workspace_bytes(const Shape& s) {
+  const int64_t n = tensor_elems(s);
+  if (n < 0 || (s.d != 64 && s.d != 128)) return 0;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  return up(size_t(n) * 4) + up(size_t(s.B) * s.H * s.N * 4);
+}
+
+inline int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                        const void* dO, const void* dq, const void* dk, const void* dv,
+                        const Shape& s, float scale, int causal,
+                        const void* ws, size_t ws_bytes) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return kErrNull;
+  int st = check_common(s, scale, causal);
+  if (st != kOk) return st;
+  const void* all[9] = {q, k, v, o, lse, dO, dq, dk, dv};
+  for (const void* p : all)
+    if (!aligned16(p)) return kErrAlign;
+  const size_t need = bwd_workspace_bytes(s);
+  if (!ws || ws_bytes < need) return kErrWorkspace;
+  if (!aligned16(ws)) return kErrAlign;
+  const size_t tb = size_t(tensor_elems(s)) * 2;
+  const size_t lb = size_t(s.B) * s.H * s.N * sizeof(float);
+  const void* ins[6] = {q, k, v, o, lse, dO};
+  const size_t insz[6] = {tb, tb, tb, tb, lb, tb};
+  const void* outs[4] = {dq, dk, dv, ws};
+  const size_t outsz[4] = {tb, tb, tb, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return kErrArg;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return kErrArg;
+  }
+  return kOk;
+}
+
+inline const char* status_string(int st) {
+  switch (st) {
+    case kOk: return "FA_OK: success";
+    case kErrNull: return "FA_ERR_NULL: a required pointer is NULL";
+    case kErrShape: return "FA_ERR_SHAPE: B, H and N must be >= 1 and each tensor < 2^31 elements";
+    case kErrHeadDim: return "FA_ERR_HEAD_DIM: head dimension d must be 64 or 128";
+    case kErrScale: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case kErrAlign: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
+    case kErrWorkspace: return "FA_ERR_WORKSPACE: workspace missing or smaller than fa_bwd_workspace_bytes()";
+    case kErrDevice: return "FA_ERR_DEVICE: the current device is not a gfx950 GPU";
+    case kErrHip: return "FA_ERR_HIP: a HIP launch or runtime call failed";
+    case kErrArg: return "FA_ERR_ARG: causal must be 0 or 1 and outputs must not alias inputs";
+    default: return "unknown fa_status";
+  }
+}
+
+}  // namespace fa
+
+#endif  // FA_VALIDATE_H_

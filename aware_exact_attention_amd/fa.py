@@ -1,0 +1,149 @@
+"""Python binding of libfa.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of ``libfa.so``; this
+module only checks tensor properties, allocates outputs with torch (device
+memory and streams are torch's), and passes raw pointers plus the current HIP
+stream through the C ABI declared in ``include/fa.h``.  There is no fallback:
+if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+_lib = None
+_lock = threading.Lock()
+
+# exported symbols and their C signatures (include/fa.h)
+_c_int, _c_float, _c_size_t, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+SIGNATURES = {
+    "fa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp]),
+    "fa_fwd_f32": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp]),
+    "fa_bwd_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    "fa_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
+                        _c_int, _vp, _c_size_t, _vp]),
+    "fa_status_string": (ctypes.c_char_p, [_c_int]),
+}
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load(path: str | None = None):
+    """Load libfa.so (once) and bind its symbols; raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or _LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is not built: run `python -m aware_exact_attention_amd.build` first")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B,H,N,d]")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: float | None = None,
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Forward attention of ``[B,H,N,d]`` tensors; returns ``(o, lse)``.
+
+    bf16 inputs run ``fa_fwd``; float32 inputs run ``fa_fwd_f32``.  ``scale``
+    defaults to ``1/sqrt(d)``.  ``out``/``lse`` may be passed preallocated.
+    """
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,N,d]")
+    B, H, N, d = q.shape
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported dtype {dtype}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dtype, (B, H, N, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", dtype, (B, H, N, d))
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, N))
+    fn = lib.fa_fwd if dtype == torch.bfloat16 else lib.fa_fwd_f32
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+            float(scale), int(bool(causal)), _stream())
+    if st != 0:
+        raise FAError(st, "fa_fwd" if dtype == torch.bfloat16 else "fa_fwd_f32")
+    return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, workspace=None, out=None):
+    """Backward attention (bf16); returns ``(dq, dk, dv)``.
+
+    ``o`` and ``lse`` must be what ``fwd`` returned for the same inputs, scale
+    and causal flag.  ``workspace`` (a uint8 GPU tensor of at least
+    ``bwd_workspace_bytes`` bytes) is allocated if not given; ``out`` may hold
+    preallocated ``(dq, dk, dv)``.
+    """
+    lib = load()
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    _check(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            _check(t, n, torch.bfloat16, (B, H, N, d))
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8)
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                    workspace.data_ptr(), workspace.numel(), _stream())
+    if st != 0:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,179 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one synthetic batch:
+fa_fwd (O and LSE) followed by fa_bwd (dQ, dK, dV by recomputation), at
+B=1, H=8, N=16384, d=128, bf16, non-causal -- the shape of the pages'
+sequence-length benchmark at its largest N (FlashAttention-2 principle and
+deployment page, benchmark section).  Inputs are resident in HBM before the
+timed region.  The forward and backward calls are bracketed by HIP events on
+the stream they run on, so their per-call durations are measured live.
+
+Prints ONE JSON line.  `value` is the algorithmic TFLOP/s of the step
+(forward 4*B*H*N^2*d plus backward 10*B*H*N^2*d, divided by the step time).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from aware_exact_attention_amd import fa  # noqa: E402
+from aware_exact_attention_amd.inputs import WORKLOADS, make_inputs, to_f64  # noqa: E402
+
+METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak at B1 H8 N16K d128; bwd TFLOP/s"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="bwd_16k", choices=sorted(WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=1, help="heads of the workload the oracle is timed on")
+    p.add_argument("--traffic-json", default=None,
+                   help="measured HBM bytes per launch {'fwd': B, 'bwd_main': B} from rocprofv3 counter runs")
+    return p.parse_args()
+
+
+def cpu_baseline(w, q, k, v, do, heads: int):
+    """Time the fp64 oracle (as it stands) on `heads` heads of the workload on the host cores."""
+    import numpy as np  # noqa: F401
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    sl = (slice(0, 1), slice(0, heads))
+    args = [to_f64(t[sl]) for t in (q, k, v, do)]
+    t0 = time.perf_counter()
+    oracle.ref_fwd(*args[:3], w.scale, w.causal)
+    t1 = time.perf_counter()
+    oracle.ref_bwd(*args, w.scale, w.causal)
+    t2 = time.perf_counter()
+    frac = heads / (w.B * w.H)
+    flop = (w.fwd_flop + w.bwd_flop) * frac
+    return {
+        "value": round(flop / (t2 - t0) / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 oracle ref_fwd + ref_bwd on {heads} of {w.B * w.H} heads of the benchmark workload "
+                  f"(N={w.N}, d={w.d}); fwd {t1 - t0:.2f} s, bwd {t2 - t1:.2f} s; TFLOP/s of that sample",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": a.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    fa.load()
+    w = WORKLOADS[a.workload]
+    q, k, v, do = make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_std, backward=True)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, workspace=ws, out=grads)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    for t in (o, lse) + grads:
+        assert torch.isfinite(t).all().item(), "non-finite output"
+
+    ms_step = (t1 - t0) * 1e3 / a.steps
+    f_ms = sum(fwd_ms) / len(fwd_ms)
+    b_ms = sum(bwd_ms) / len(bwd_ms)
+    f_tf = w.fwd_flop / (f_ms * 1e-3) / 1e12
+    b_tf = w.bwd_flop / (b_ms * 1e-3) / 1e12
+    value = (w.fwd_flop + w.bwd_flop) / (ms_step * 1e-3) / 1e12
+
+    traffic = {}
+    if a.traffic_json and os.path.exists(a.traffic_json):
+        traffic = json.load(open(a.traffic_json))
+
+    def roof(flop, ms, key):
+        ach = flop / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic.get(key)}
+
+    # the backward (2.5x the forward's FLOPs) is the dominant cost of the step
+    dominant = "bwd" if b_ms >= f_ms else "fwd"
+    r_bwd = roof(w.bwd_flop, b_ms, "bwd_main")
+    r_bwd["kernel"] = "fa_bwd: bwd_main_kernel (+ bwd_pre_kernel, bwd_dq_convert_kernel in the same event pair)"
+    r_fwd = roof(w.fwd_flop, f_ms, "fwd")
+    r_fwd["kernel"] = "fa_fwd: fwd_bf16_kernel"
+    bytes_fwd = w.B * w.H * w.N * (8 * w.d + 4)
+    bytes_bwd = w.B * w.H * w.N * (16 * w.d + 12)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"attention fwd+bwd B{w.B} H{w.H} N{w.N} d{w.d} bf16 "
+                               f"{'causal' if w.causal else 'non-causal'}, seeded N(0,1) inputs",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed},
+        "fwd": {"ms": round(f_ms, 4), "tflops": round(f_tf, 2), "frac_peak": round(f_tf / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_bytes": bytes_fwd,
+                "pages_a100_context": "pages: 28.5 ms (38.6 TFLOP/s derived) on an A100 at this shape, forward only"},
+        "bwd": {"ms": round(b_ms, 4), "tflops": round(b_tf, 2), "frac_peak": round(b_tf / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_bytes": bytes_bwd},
+        "roofline": r_bwd if dominant == "bwd" else r_fwd,
+        "roofline_fwd": r_fwd,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, a.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

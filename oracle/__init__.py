@@ -4,4 +4,4 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import anything from this package.  The HIP library and its
 Python binding never do, and this package imports nothing from them.
 """
-from .ref import ref_bwd, ref_bwd_delta, ref_fwd, ref_probs  # noqa: F401
+from .ref import ref_bwd, ref_bwd_delta, ref_fwd, ref_fwd_rows, ref_probs  # noqa: F401

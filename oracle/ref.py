@@ -86,6 +86,23 @@ def ref_fwd(q, k, v, scale: float, causal: bool):
     return o, lse
 
 
+def ref_fwd_rows(q, k, v, scale: float, causal: bool, rows):
+    """Forward attention of one head ``[N,d]`` for the query rows ``rows`` only.
+
+    Query rows are independent in the definition, so this is the same
+    computation as ``ref_fwd`` restricted to a subset of rows (used to check
+    outputs of workloads too large to materialise in full).  Returns
+    ``(O[rows], LSE[rows])`` in float64.
+    """
+    q, k, v = _as_f64(q, k, v)
+    rows = np.asarray(rows, dtype=np.int64)
+    s = scale * (q[rows] @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > rows[:, None], -np.inf, s)
+    p, m, l = _softmax_rows(s)
+    return p @ v, m + np.log(l)
+
+
 def ref_probs(q, k, scale: float, causal: bool):
     """The attention probabilities ``P`` of every head, ``[B,H,N,N]`` (small inputs only)."""
     q, k = _as_f64(q, k)

@@ -1,0 +1,181 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol that
+include/fa.h declares, and rejects invalid arguments before touching the GPU.
+
+No call here reaches a kernel: every call fails validation, which runs before
+the device check and before anything is enqueued.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+LIB = os.path.join(ROOT, "aware_exact_attention_amd", "libfa.so")
+
+ST = {"OK": 0, "NULL": -1, "SHAPE": -2, "HEAD_DIM": -3, "SCALE": -4, "ALIGN": -5, "WORKSPACE": -6,
+      "DEVICE": -7, "HIP": -8, "ARG": -9}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import aware_exact_attention_amd.build as b
+        b.build()
+    from aware_exact_attention_amd import fa
+    return fa.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_bytes", "fa_bwd",
+                                           "fa_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from aware_exact_attention_amd import fa
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, f"{name} not exported by libfa.so"
+        assert name in fa.SIGNATURES
+        assert hasattr(lib, name)
+
+
+def test_status_codes_match_header(lib):
+    text = open(HEADER).read()
+    for name, val in ST.items():
+        assert re.search(rf"FA_(ERR_)?{name}\s*=\s*{val}\b", text), name
+    for val in ST.values():
+        s = lib.fa_status_string(val).decode()
+        assert s and s != "unknown fa_status"
+    assert lib.fa_status_string(12345).decode() == "unknown fa_status"
+
+
+class _Buf:
+    """Host buffers used only as distinct, aligned, non-null addresses."""
+
+    def __init__(self, nbytes):
+        self.raw = ctypes.create_string_buffer(nbytes + 64)
+        a = ctypes.addressof(self.raw)
+        self.ptr = (a + 15) // 16 * 16
+
+
+def _fwd_args(B=1, H=1, N=8, d=64):
+    bufs = [_Buf(B * H * N * d * 4) for _ in range(4)] + [_Buf(B * H * N * 4)]
+    return bufs, [b.ptr for b in bufs]
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+def test_fwd_validation(lib, fn):
+    f = getattr(lib, fn)
+    bufs, (q, k, v, o, l) = _fwd_args()
+    assert f(None, k, v, o, l, 1, 1, 8, 64, 0.125, 0, None) == ST["NULL"]
+    assert f(q, k, v, o, None, 1, 1, 8, 64, 0.125, 0, None) == ST["NULL"]
+    assert f(q, k, v, o, l, 0, 1, 8, 64, 0.125, 0, None) == ST["SHAPE"]
+    assert f(q, k, v, o, l, 1, -1, 8, 64, 0.125, 0, None) == ST["SHAPE"]
+    assert f(q, k, v, o, l, 1, 1, 0, 64, 0.125, 0, None) == ST["SHAPE"]
+    assert f(q, k, v, o, l, 1 << 12, 1 << 10, 1 << 10, 64, 0.125, 0, None) == ST["SHAPE"]
+    assert f(q, k, v, o, l, 1, 1, 8, 96, 0.125, 0, None) == ST["HEAD_DIM"]
+    assert f(q, k, v, o, l, 1, 1, 8, 256, 0.125, 0, None) == ST["HEAD_DIM"]
+    assert f(q, k, v, o, l, 1, 1, 8, 64, float("nan"), 0, None) == ST["SCALE"]
+    assert f(q, k, v, o, l, 1, 1, 8, 64, float("inf"), 0, None) == ST["SCALE"]
+    assert f(q, k, v, o, l, 1, 1, 8, 64, 0.0, 0, None) == ST["SCALE"]
+    assert f(q, k, v, o, l, 1, 1, 8, 64, -0.125, 0, None) == ST["SCALE"]
+    assert f(q, k, v, o, l, 1, 1, 8, 64, 0.125, 2, None) == ST["ARG"]
+    assert f(q + 2, k, v, o, l, 1, 1, 8, 64, 0.125, 0, None) == ST["ALIGN"]
+    assert f(q, k, v, o, l + 4, 1, 1, 8, 64, 0.125, 0, None) == ST["ALIGN"]
+    assert f(q, k, v, q, l, 1, 1, 8, 64, 0.125, 0, None) == ST["ARG"]  # output aliases input
+    assert f(q, k, v, o, o, 1, 1, 8, 64, 0.125, 0, None) == ST["ARG"]  # lse aliases output
+
+
+def test_bwd_workspace_bytes(lib):
+    n = 2 * 3 * 100 * 128
+    want = (n * 4 + 255) // 256 * 256 + (2 * 3 * 100 * 4 + 255) // 256 * 256
+    assert lib.fa_bwd_workspace_bytes(2, 3, 100, 128) == want
+    assert lib.fa_bwd_workspace_bytes(0, 3, 100, 128) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 100, 80) == 0
+
+
+def test_bwd_validation(lib):
+    B, H, N, d = 1, 2, 16, 64
+    bufs = [_Buf(B * H * N * d * 2) for _ in range(9)]
+    q, k, v, o, lse, do, dq, dk, dv = [b.ptr for b in bufs]
+    need = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    wsb = _Buf(need)
+    ws = wsb.ptr
+    base = [q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, 0.125, 1, ws, need, None]
+
+    def call(**ch):
+        a = list(base)
+        names = ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "B", "H", "N", "d", "scale", "causal", "ws",
+                 "wsb", "stream"]
+        for kk, vv in ch.items():
+            a[names.index(kk)] = vv
+        return lib.fa_bwd(*a)
+
+    assert call(do=None) == ST["NULL"]
+    assert call(dk=None) == ST["NULL"]
+    assert call(N=0) == ST["SHAPE"]
+    assert call(d=32) == ST["HEAD_DIM"]
+    assert call(scale=float("nan")) == ST["SCALE"]
+    assert call(causal=-1) == ST["ARG"]
+    assert call(ws=None) == ST["WORKSPACE"]
+    assert call(wsb=need - 1) == ST["WORKSPACE"]
+    assert call(dq=dq + 8) == ST["ALIGN"]
+    assert call(dk=dq) == ST["ARG"]          # two outputs alias
+    assert call(dv=v) == ST["ARG"]           # output aliases an input
+    assert call(ws=dq) == ST["ARG"]          # workspace aliases an output
+
+
+def test_validate_header_with_gxx(tmp_path):
+    """Host unit test of fa_validate.h compiled by g++ (no HIP, no GPU)."""
+    src = tmp_path / "t.cpp"
+    src.write_text(r'''
+#include "fa_validate.h"
+#include <cstdio>
+#include <cmath>
+using namespace fa;
+static int fails = 0;
+#define EXPECT(x) do { if (!(x)) { std::printf("FAIL line %d: %s\n", __LINE__, #x); ++fails; } } while (0)
+int main() {
+  alignas(16) static char mem[9][8192];
+  alignas(16) static char ws[1 << 16];
+  Shape s{1, 2, 16, 64};
+  EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 0, 2) == kOk);
+  EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 1, 4) == kOk);
+  EXPECT(validate_fwd(nullptr, mem[1], mem[2], mem[3], mem[4], s, 0.125f, 0, 2) == kErrNull);
+  EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], Shape{1, 2, 16, 65}, 0.125f, 0, 2) == kErrHeadDim);
+  EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], Shape{1, 0, 16, 64}, 0.125f, 0, 2) == kErrShape);
+  EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], s, NAN, 0, 2) == kErrScale);
+  EXPECT(validate_fwd(mem[0] + 1, mem[1], mem[2], mem[3], mem[4], s, 0.125f, 0, 2) == kErrAlign);
+  EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[0] + 16, mem[4], s, 0.125f, 0, 2) == kErrArg);
+  EXPECT(tensor_elems(Shape{1024, 1024, 1024, 2}) == -1);
+  EXPECT(tensor_elems(Shape{2, 3, 5, 64}) == 1920);
+  size_t need = bwd_workspace_bytes(s);
+  EXPECT(need == 8192 + 256);
+  EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s, 0.125f, 1,
+                      ws, sizeof ws) == kOk);
+  EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s, 0.125f, 1,
+                      ws, need - 1) == kErrWorkspace);
+  EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[6], mem[8], s, 0.125f, 1,
+                      ws, sizeof ws) == kErrArg);
+  EXPECT(overlaps(mem[0], 16, mem[0] + 15, 1) && !overlaps(mem[0], 16, mem[0] + 16, 1));
+  return fails ? 1 : 0;
+}
+''')
+    exe = tmp_path / "t"
+    inc = os.path.join(ROOT, "aware_exact_attention_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-fsanitize=address,undefined", "-I", inc, str(src),
+                    "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr

@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Inputs are the seeded workloads of ``aware_exact_attention_amd.inputs``; the
+GPU receives the bf16 (or fp32) tensors and the oracle the same values widened
+to float64.  Outputs are pre-filled with NaN so that an element the kernels
+never write fails the comparison.
+
+Tolerances (written here, derived in the design notes):
+* O, bf16 path: max-abs <= 2e-2 and mean-abs <= 2e-3; fp32 path: max-abs <= 1e-5.
+* LSE: max-abs <= 1e-3 (bf16 path), <= 1e-5 (fp32 path).
+* dQ, dK, dV (bf16 path): max-abs <= 2e-2 * max|ref| and mean-abs <= 1e-2 * mean|ref|
+  (bf16 rounding of P, dS and of the outputs is 2^-9 relative each).
+
+Small sizes are compared element by element in full.  Full-size workloads are
+run in the same launch configuration the benchmark times and compared on
+sampled rows (forward: every head, rows at the start, the end, tile
+boundaries and random positions) or sampled heads (backward: all outputs of
+the sampled heads).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from aware_exact_attention_amd.inputs import WORKLOADS, make_inputs, to_f64, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN = 2e-2, 2e-3
+LSE_BF16 = 1e-3
+F32_TOL = 1e-5
+G_MAX_REL, G_MEAN_REL = 2e-2, 1e-2
+
+REPORT = os.environ.get("FA_PARITY_REPORT")
+
+
+def _report(**kw):
+    print(json.dumps(kw), flush=True)
+    if REPORT:
+        with open(REPORT, "a") as f:
+            f.write(json.dumps(kw) + "\n")
+
+
+def _gpu(*ts):
+    return [t.cuda() for t in ts]
+
+
+def _fwd(fa, q, k, v, causal, scale):
+    qd, kd, vd = _gpu(q, k, v)
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full(qd.shape[:3], float("nan"), device="cuda", dtype=torch.float32)
+    fa.fwd(qd, kd, vd, causal=causal, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _np(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def check_o(name, got, ref, fp32=False):
+    assert np.isfinite(got).all(), f"{name}: non-finite output (unwritten or NaN)"
+    err = np.abs(got - ref)
+    _report(check=name, what="O", max_abs=float(err.max()), mean_abs=float(err.mean()))
+    if fp32:
+        assert err.max() <= F32_TOL, f"{name}: O max-abs {err.max():.3e} > {F32_TOL}"
+    else:
+        assert err.max() <= O_MAX, f"{name}: O max-abs {err.max():.3e} > {O_MAX}"
+        assert err.mean() <= O_MEAN, f"{name}: O mean-abs {err.mean():.3e} > {O_MEAN}"
+
+
+def check_lse(name, got, ref, fp32=False):
+    assert np.isfinite(got).all(), f"{name}: non-finite LSE"
+    err = np.abs(got - ref)
+    tol = F32_TOL if fp32 else LSE_BF16
+    _report(check=name, what="LSE", max_abs=float(err.max()))
+    assert err.max() <= tol, f"{name}: LSE max-abs {err.max():.3e} > {tol}"
+
+
+def check_grad(name, what, got, ref):
+    assert np.isfinite(got).all(), f"{name}: non-finite {what}"
+    err = np.abs(got - ref)
+    mref, aref = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    _report(check=name, what=what, max_abs=float(err.max()), mean_abs=float(err.mean()),
+            ref_max=mref, ref_mean=aref)
+    assert err.max() <= G_MAX_REL * mref + 1e-6, f"{name}: {what} max-abs {err.max():.3e} (ref max {mref:.3e})"
+    assert err.mean() <= G_MEAN_REL * aref + 1e-7, f"{name}: {what} mean-abs {err.mean():.3e} (ref mean {aref:.3e})"
+
+
+def sample_rows(N, rng, tile=128, extra=192):
+    rows = set(range(min(N, 40))) | set(range(max(0, N - 40), N))
+    for b in range(tile, N, tile * max(1, N // tile // 16)):
+        rows |= {b - 1, b, min(N - 1, b + 1)}
+    rows |= set(rng.choice(N, size=min(N, extra), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+# --------------------------------------------------------------------------
+# forward: small sizes, full comparison
+# --------------------------------------------------------------------------
+
+def test_tiny_f32(gpu_lib):
+    w = WORKLOADS["tiny_f32"]
+    q, k, v = workload_inputs(w)
+    o, lse = _fwd(gpu_lib, q, k, v, w.causal, w.scale)
+    ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), w.scale, w.causal)
+    check_o("tiny_f32", _np(o), ro, fp32=True)
+    check_lse("tiny_f32", _np(lse), rl, fp32=True)
+
+
+@pytest.mark.parametrize("N", [1, 3, 31, 100, 129, 1000, 4097])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_bf16(gpu_lib, N, d, causal):
+    q, k, v = make_inputs(1, 2, N, d, "bf16", seed=100 + N)
+    scale = d ** -0.5
+    o, lse = _fwd(gpu_lib, q, k, v, causal, scale)
+    ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), scale, causal)
+    check_o(f"ragged_bf16 N={N} d={d} causal={causal}", _np(o), ro)
+    check_lse(f"ragged_bf16 N={N} d={d} causal={causal}", _np(lse), rl)
+
+
+@pytest.mark.parametrize("N", [1, 5, 63, 65, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_f32(gpu_lib, N, d, causal):
+    q, k, v = make_inputs(2, 1, N, d, "f32", seed=200 + N)
+    scale = d ** -0.5
+    o, lse = _fwd(gpu_lib, q, k, v, causal, scale)
+    ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), scale, causal)
+    check_o(f"ragged_f32 N={N} d={d} causal={causal}", _np(o), ro, fp32=True)
+    check_lse(f"ragged_f32 N={N} d={d} causal={causal}", _np(lse), rl, fp32=True)
+
+
+def test_other_scale_and_peaked_rows(gpu_lib):
+    """A scale other than 1/sqrt(d) and rows dominated by one key."""
+    q, k, v = make_inputs(1, 2, 257, 128, "bf16", seed=300, qk_std=3.0)
+    o, lse = _fwd(gpu_lib, q, k, v, True, 0.3)
+    ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), 0.3, True)
+    check_o("scale0.3_peaked", _np(o), ro)
+    check_lse("scale0.3_peaked", _np(lse), rl)
+
+
+@pytest.mark.parametrize("name", ["gpt2", "gpt2_causal"])
+def test_gpt2_shape(gpu_lib, name):
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    o, lse = _fwd(gpu_lib, q, k, v, w.causal, w.scale)
+    ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), w.scale, w.causal)
+    check_o(name, _np(o), ro)
+    check_lse(name, _np(lse), rl)
+
+
+def test_forward_deterministic(gpu_lib):
+    q, k, v = _gpu(*make_inputs(2, 4, 1000, 128, "bf16", seed=7))
+    o1, l1 = gpu_lib.fwd(q, k, v, causal=True)
+    o2, l2 = gpu_lib.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# --------------------------------------------------------------------------
+# forward: full-size workloads, sampled rows of every head
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["sweep_2k", "sweep_4k", "sweep_8k", "sweep_16k", "stress_causal"])
+def test_full_size_forward_sampled(gpu_lib, name):
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    o, lse = _fwd(gpu_lib, q, k, v, w.causal, w.scale)
+    o, lse = _np(o), _np(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    qn, kn, vn = to_f64(q), to_f64(k), to_f64(v)
+    rng = np.random.default_rng(w.seed)
+    errs_o, errs_l = [], []
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = sample_rows(w.N, rng)
+            ro, rl = oracle.ref_fwd_rows(qn[b, h], kn[b, h], vn[b, h], w.scale, w.causal, rows)
+            errs_o.append(np.abs(o[b, h, rows] - ro).ravel())
+            errs_l.append(np.abs(lse[b, h, rows] - rl))
+    eo, el = np.concatenate(errs_o), np.concatenate(errs_l)
+    _report(check=name, what="O(sampled rows)", max_abs=float(eo.max()), mean_abs=float(eo.mean()),
+            rows=int(el.size))
+    _report(check=name, what="LSE(sampled rows)", max_abs=float(el.max()))
+    assert eo.max() <= O_MAX and eo.mean() <= O_MEAN
+    assert el.max() <= LSE_BF16
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+
+def _bwd_case(fa, q, k, v, do, causal, scale):
+    qd, kd, vd, dod = _gpu(q, k, v, do)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale)
+    outs = tuple(torch.full_like(qd, float("nan")) for _ in range(3))
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, dod, causal=causal, scale=scale, out=outs)
+    torch.cuda.synchronize()
+    return _np(o), _np(lse), _np(dq), _np(dk), _np(dv)
+
+
+@pytest.mark.parametrize("N", [1, 33, 130, 300, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_small(gpu_lib, N, d, causal):
+    q, k, v, do = make_inputs(1, 2, N, d, "bf16", seed=400 + N, backward=True)
+    scale = d ** -0.5
+    _, _, dq, dk, dv = _bwd_case(gpu_lib, q, k, v, do, causal, scale)
+    rq, rk, rv = oracle.ref_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal)
+    tag = f"bwd N={N} d={d} causal={causal}"
+    check_grad(tag, "dQ", dq, rq)
+    check_grad(tag, "dK", dk, rk)
+    check_grad(tag, "dV", dv, rv)
+
+
+@pytest.mark.parametrize("name,heads", [("fwd_bwd_causal", [(0, 0), (1, 7), (3, 15)]), ("bwd_16k", [(0, 5)])])
+def test_full_size_backward_sampled_heads(gpu_lib, name, heads):
+    w = WORKLOADS[name]
+    q, k, v, do = workload_inputs(w)
+    o, lse, dq, dk, dv = _bwd_case(gpu_lib, q, k, v, do, w.causal, w.scale)
+    for arr in (o, lse, dq, dk, dv):
+        assert np.isfinite(arr).all()
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        args = [to_f64(t[sl]) for t in (q, k, v, do)]
+        ro, rl = oracle.ref_fwd(*args[:3], w.scale, w.causal)
+        rq, rk, rv = oracle.ref_bwd(*args, w.scale, w.causal)
+        tag = f"{name} head=({b},{h})"
+        check_o(tag, o[sl], ro)
+        check_lse(tag, lse[sl], rl)
+        check_grad(tag, "dQ", dq[sl], rq)
+        check_grad(tag, "dK", dk[sl], rk)
+        check_grad(tag, "dV", dv[sl], rv)
+
+
+def test_bwd_workspace_reuse_and_stale_contents(gpu_lib):
+    """A workspace holding garbage from an earlier, larger call gives the same result."""
+    q, k, v, do = _gpu(*make_inputs(1, 2, 700, 128, "bf16", seed=500, backward=True))
+    ws = torch.full((gpu_lib.bwd_workspace_bytes(2, 4, 2000, 128),), 0x7f, dtype=torch.uint8, device="cuda")
+    o, lse = gpu_lib.fwd(q, k, v, causal=True)
+    a = gpu_lib.bwd(q, k, v, o, lse, do, causal=True, workspace=ws)
+    b = gpu_lib.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert (x.float() - y.float()).abs().max().item() <= 2e-2 * y.float().abs().max().item()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])  # dK, dV have no atomics

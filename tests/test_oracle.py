@@ -155,6 +155,10 @@ def pin_torch_sdpa(R):
         if causal:
             s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
         np.testing.assert_allclose(lse, torch.logsumexp(s, -1).numpy(), rtol=0, atol=1e-13)
+        rows = [0, 1, 7, 44, 20]
+        orow, lrow = R.ref_fwd_rows(q[1, 2], k[1, 2], v[1, 2], scale, causal, rows)
+        np.testing.assert_allclose(orow, to.numpy()[1, 2, rows], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lrow, torch.logsumexp(s, -1).numpy()[1, 2, rows], rtol=0, atol=1e-13)
 
 
 def _loss(R, q, k, v, do, scale, causal):
