@@ -9,6 +9,7 @@ namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -43,6 +44,43 @@ template <int UNITS>
 __device__ __forceinline__ int swz(int row, int unit) {
   if constexpr (UNITS == 16) return unit ^ (row & 15);
   else return unit ^ ((row ^ (row >> 3)) & 7);
+}
+
+// Swizzle of the 16-byte units of one row of a row-major K or V tile in LDS
+// (d = 128: 16 units per 256-byte row; d = 64: 8 units per 128-byte row).
+// Physical unit = logical unit ^ tile_swz<D>(row).  The tables were chosen so
+// that both access patterns of the tiles hit distinct banks, whether the LDS
+// serves 16 lanes x 16 bytes or 8 lanes x 16 bytes per cycle:
+//  * 128-bit row reads: 32 consecutive rows, one logical unit;
+//  * ds_read_b64_tr_b16: per 16-lane group, 4 consecutive rows x 32 bytes.
+template <int D>
+__device__ __forceinline__ int tile_swz(int row) {
+  const int r = row & 15;
+  if constexpr (D == 128) {
+    const int i = r & 3;  // {0, 6, 10, 12}[i] ^ (r / 4)
+    const int p = ((i >> 1) << 3) | ((i & 1) << 2) | (((i ^ (i >> 1)) & 1) << 1);
+    return p ^ (r >> 2);
+  } else {
+    return ((2 * (r & 3)) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1);
+  }
+}
+
+// Buffer resource over `bytes` bytes at `base`: loads past the end return 0,
+// stores past the end are dropped (gfx9 descriptor word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes
+// lds[16*l .. 16*l+15] (the LDS address is wave-uniform).  The host pass only
+// emits the kernel's launch stub, so the builtin is compiled for the device
+// alone (its presence in the host pass suppresses the stub).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voffset, 0, 0, 0);
+#endif
 }
 
 // Pack two fp32 values into two bf16 (round to nearest even) in one dword.

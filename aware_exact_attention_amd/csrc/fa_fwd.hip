@@ -40,28 +40,12 @@ struct FwdTile {
   static constexpr int DB = D / 32;               // 32-column blocks of O
   static constexpr int KB = BC / 32;              // 32-key blocks of S
   static constexpr int PS = BC / 16;              // 16-key k steps of P V
-  static constexpr int K_UNITS = D / 8;           // 16-byte units per K row
-  static constexpr int V_UNITS = BC / 8;          // 16-byte units per V^T row
-  static constexpr int K_BYTES = BC * D * 2;
-  static constexpr int V_BYTES = D * BC * 2;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int K_LOADS = BC * K_UNITS / NT;   // 16-byte K loads per thread per tile
-  static constexpr int V_PIECES = (BC / 4) * (D / 8); // (4 keys x 8 columns) pieces of V per tile
-  static_assert(BC * K_UNITS % NT == 0, "K tile must split evenly over the threads");
-  static_assert(V_PIECES <= NT, "one V piece per thread at most");
+  static constexpr int RS = D * 2;                // bytes per tile row (K and V alike)
+  static constexpr int TILE = BC * RS;            // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;          // K tile then V tile
+  static constexpr int LPW = TILE / 1024 / NW;    // 1 KiB direct-to-LDS loads per wave per tile
+  static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
-
-// Byte offset of V^T[dcol][key] piece (4 keys starting at key chunk kc) in the
-// LDS V^T tile.  Within every group of 16 keys the four 4-key chunks are
-// stored in the order (0, 2 | 1, 3) so that one 16-byte unit holds exactly
-// the 8 keys that one lane feeds to one PV MFMA step.
-template <int D>
-__device__ __forceinline__ int vt_offset(int dcol, int kc) {
-  using T = FwdTile<D>;
-  const int g = kc >> 2, cc = kc & 3;
-  const int unit = 2 * g + (cc & 1);
-  return dcol * (T::BC * 2) + swz<T::V_UNITS>(dcol, unit) * 16 + (cc >> 1) * 8;
-}
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
@@ -69,31 +53,34 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                 int N, int Tr, float c) {
   using T = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
+  const int l32 = lane & 31;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / Tr;
   int it = tile - bh * Tr;
   if (CAUSAL) it = Tr - 1 - it;  // longest rows first
   const int q0 = it * T::BR;
   const size_t head = size_t(bh) * N * D;
-  const __bf16* Qh = Q + head;
   const __bf16* Kh = K + head;
   const __bf16* Vh = V + head;
+  const int head_bytes = N * T::RS;
 
-  // Q fragment (B operand of S^T = K Q^T): query row lane%32 of this wave,
-  // columns 16*s + 8*half .. +7 for k step s.
+  // Q fragment (B operand of S^T = K Q^T): row qrow, columns 16*s + 8*half .. +7.
+  // Rows past N read as zero (buffer bounds).
   const int wq0 = q0 + wave * 32;
-  const int qrow = wq0 + (lane & 31);
+  const int qrow = wq0 + l32;
   bf16x8 qf[T::KS];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head, head_bytes);
 #pragma unroll
-  for (int s = 0; s < T::KS; ++s) {
-    if (qrow < N) qf[s] = *reinterpret_cast<const bf16x8*>(Qh + size_t(qrow) * D + 16 * s + 8 * half);
-    else qf[s] = bf16x8{};
+    for (int s = 0; s < T::KS; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rq, qrow * T::RS + (16 * s + 8 * half) * 2, 0, 0));
   }
 
   const int Tc = (N + T::BC - 1) / T::BC;
@@ -103,78 +90,77 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   int nt_w = nt;
   if (CAUSAL && wave_active) nt_w = min(nt, (min(wq0 + 32, N) - 1) / T::BC + 1);
 
+  // Direct-to-LDS tile loads: load i of this wave fills LDS bytes
+  // [(wave*LPW + i) KiB, +1 KiB) of the tile; lane l brings the 16 bytes that
+  // belong at byte 16*l of that range under the swizzle.
+  int goff[T::LPW];
+#pragma unroll
+  for (int i = 0; i < T::LPW; ++i) {
+    const int p = (wave * T::LPW + i) * 1024 + 16 * lane;
+    const int row = p / T::RS, pu = (p % T::RS) / 16;
+    goff[i] = row * T::RS + ((pu ^ tile_swz<D>(row)) * 16);
+  }
+  auto issue_loads = [&](int j, int stage) {
+    const int key0 = j * T::BC;
+    const int bytes = (N - key0) * T::RS;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + size_t(key0) * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + size_t(key0) * D, bytes);
+    char* kdst = smem + stage * T::STAGE + wave * T::LPW * 1024;
+#pragma unroll
+    for (int i = 0; i < T::LPW; ++i)
+      load_lds16(rk, kdst + i * 1024, goff[i]);
+#pragma unroll
+    for (int i = 0; i < T::LPW; ++i)
+      load_lds16(rv, kdst + T::TILE + i * 1024, goff[i]);
+  };
+
+  // LDS read offsets (bytes within a stage).
+  // K rows kb*32 + l32, logical unit 2*st + half.
+  int kof[T::KS];
+#pragma unroll
+  for (int st = 0; st < T::KS; ++st) kof[st] = l32 * T::RS + (((2 * st + half) ^ tile_swz<D>(l32)) * 16);
+  // V transposing reads: in 16-lane group g (lane t), row 4*(g/2) + 8*r2 + t/4
+  // (+16 per PV k step), columns 32*b + 16*(g%2) + 4*(t%4) .. +3.
+  int vof[T::DB][2];
+  {
+    const int g = lane >> 4, t = lane & 15;
+#pragma unroll
+    for (int b = 0; b < T::DB; ++b)
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const int row = 4 * (g >> 1) + 8 * r2 + (t >> 2);
+        const int col = 32 * b + 16 * (g & 1) + 4 * (t & 3);
+        vof[b][r2] = T::TILE + row * T::RS + (((col >> 3) ^ tile_swz<D>(row)) * 16) + (col & 7) * 2;
+      }
+  }
+
   f32x16 o[T::DB];
 #pragma unroll
   for (int b = 0; b < T::DB; ++b) o[b] = f32x16{};
   float m = -INFINITY;  // running max of scale*log2(e)*score
-  float l = 0.f;        // running sum of this lane's half of the keys
-
-  u32x4 kst[T::K_LOADS];
-  u32x4 vst[4];
-  const int v_dc = tid % (D / 8), v_kc = tid / (D / 8);
-  const bool v_loader = tid < T::V_PIECES;
-
-  auto gload = [&](int j) {
-    const int key0 = j * T::BC;
-#pragma unroll
-    for (int r = 0; r < T::K_LOADS; ++r) {
-      const int idx = tid + r * T::NT;
-      const int row = idx / T::K_UNITS, unit = idx % T::K_UNITS;
-      const int key = key0 + row;
-      kst[r] = key < N ? *reinterpret_cast<const u32x4*>(Kh + size_t(key) * D + unit * 8) : u32x4{};
-    }
-    if (v_loader) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + v_kc * 4 + r;
-        vst[r] = key < N ? *reinterpret_cast<const u32x4*>(Vh + size_t(key) * D + v_dc * 8) : u32x4{};
-      }
-    }
-  };
-
-  auto lds_store = [&](int buf) {
-    char* base = smem + buf * T::STAGE;
-#pragma unroll
-    for (int r = 0; r < T::K_LOADS; ++r) {
-      const int idx = tid + r * T::NT;
-      const int row = idx / T::K_UNITS, unit = idx % T::K_UNITS;
-      *reinterpret_cast<u32x4*>(base + row * (D * 2) + swz<T::K_UNITS>(row, unit) * 16) = kst[r];
-    }
-    if (v_loader) {
-      char* vb = base + T::K_BYTES;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dword w of each loaded row holds columns 2w (low half) and 2w+1 (high half)
-        const unsigned a0 = vst[0][w], a1 = vst[1][w], a2 = vst[2][w], a3 = vst[3][w];
-        u32x2 lo, hi;
-        lo[0] = (a0 & 0xffffu) | (a1 << 16);
-        lo[1] = (a2 & 0xffffu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        const int dcol = v_dc * 8 + 2 * w;
-        *reinterpret_cast<u32x2*>(vb + vt_offset<D>(dcol, v_kc)) = lo;
-        *reinterpret_cast<u32x2*>(vb + vt_offset<D>(dcol + 1, v_kc)) = hi;
-      }
-    }
-  };
+  float l = 0.f;        // running sum over this lane's half of the keys
 
   auto compute = [&](int j, const char* base) {
-    const char* Ks = base;
-    const char* Vs = base + T::K_BYTES;
-    // S^T block kb: rows = keys kb*32 + (lane%32), cols = this wave's queries
-    f32x16 s[T::KB];
+    // ---- S^T = K_j Q^T: two independent 32-key chains, K operands read one step ahead
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(base + kof[0]);
+    bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(base + kof[0] + 32 * T::RS);
 #pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb) {
-      s[kb] = f32x16{};
-      const int row = kb * 32 + (lane & 31);
-#pragma unroll
-      for (int st = 0; st < T::KS; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Ks + row * (D * 2) + swz<T::K_UNITS>(row, 2 * st + half) * 16);
-        s[kb] = mfma32(a, qf[st], s[kb]);
+    for (int st = 0; st < T::KS; ++st) {
+      bf16x8 kn0, kn1;
+      if (st + 1 < T::KS) {
+        kn0 = *reinterpret_cast<const bf16x8*>(base + kof[st + 1]);
+        kn1 = *reinterpret_cast<const bf16x8*>(base + kof[st + 1] + 32 * T::RS);
+      }
+      s0 = mfma32(ka0, qf[st], s0);
+      s1 = mfma32(ka1, qf[st], s1);
+      if (st + 1 < T::KS) {
+        ka0 = kn0;
+        ka1 = kn1;
       }
     }
-    // masks: keys past N (ragged tail) and, if causal, keys after the query
+    f32x16 s[2] = {s0, s1};
+    // ---- masks: keys past N and, if causal, keys after the query
     const int key0 = j * T::BC;
     bool need = key0 + T::BC > N;
     if (CAUSAL) need = need || (key0 + T::BC - 1 > wq0);
@@ -187,7 +173,7 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
         }
     }
-    // running max (scale > 0, so max(score)*c == max(score*c))
+    // ---- online softmax (scale > 0, so max(score)*c == max(score*c))
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
@@ -195,10 +181,9 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, wave_swap32(mx));
     const float m_new = fmaxf(m, mx * c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // row with nothing visible yet
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet in this row
     const float alpha = exp2_fast(m - m_use);
     m = m_new;
-    // probabilities, this lane's share of the row sum, bf16 P^T fragments
     float rs = 0.f;
     bf16x8 pb[T::PS];
 #pragma unroll
@@ -214,33 +199,52 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
       for (int b = 0; b < T::DB; ++b) o[b] *= alpha;
     }
-    // O^T block b += V^T[b*32 .. +32][keys] * P^T
+    // ---- O^T += V_j^T P^T: DB independent chains; V^T operands come from two
+    // transposing reads of the row-major V tile, one (b, ps) ahead
+    auto vread = [&](int b, int ps) {
+      const char* vb = base + ps * 16 * T::RS;
+      const bf16x4 lo = __builtin_bit_cast(
+          bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(vb + vof[b][0])));
+      const bf16x4 hi = __builtin_bit_cast(
+          bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(vb + vof[b][1])));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 va = vread(0, 0);
 #pragma unroll
-    for (int b = 0; b < T::DB; ++b) {
-      const int dcol = b * 32 + (lane & 31);
+    for (int ps = 0; ps < T::PS; ++ps)
 #pragma unroll
-      for (int ps = 0; ps < T::PS; ++ps) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Vs + dcol * (T::BC * 2) + swz<T::V_UNITS>(dcol, 2 * ps + half) * 16);
-        o[b] = mfma32(a, pb[ps], o[b]);
+      for (int b = 0; b < T::DB; ++b) {
+        const int nb = (b + 1 < T::DB) ? b + 1 : 0;
+        const int nps = (b + 1 < T::DB) ? ps : ps + 1;
+        bf16x8 vn;
+        if (nps < T::PS) vn = vread(nb, nps);
+        o[b] = mfma32(va, pb[ps], o[b]);
+        if (nps < T::PS) va = vn;
       }
-    }
   };
 
-  gload(0);
-  lds_store(0);
-  __syncthreads();
-  for (int j = 0; j < nt; ++j) {
-    if (j + 1 < nt) gload(j + 1);
-    if (wave_active && j < nt_w) compute(j, smem + (j & 1) * T::STAGE);
-    if (j + 1 < nt) lds_store((j + 1) & 1);
+  auto step = [&](int j, int stage) {
+    if (j + 1 < nt) issue_loads(j + 1, stage ^ 1);
+    if (wave_active && j < nt_w) compute(j, smem + stage * T::STAGE);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j+1 have landed
     __syncthreads();
-  }
+  };
 
-  if (!wave_active || qrow >= N) return;
+  issue_loads(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < nt; j += 2) {
+    step(j, 0);
+    step(j + 1, 1);
+  }
+  if (j < nt) step(j, 0);
+
+  if (!wave_active) return;
   const float lt = l + wave_swap32(l);
   const float inv = 1.f / lt;
-  __bf16* Orow = O + head + size_t(qrow) * D;
+  // rows past N are dropped by the buffer bounds
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head, head_bytes);
 #pragma unroll
   for (int b = 0; b < T::DB; ++b)
 #pragma unroll
@@ -248,9 +252,9 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       u32x2 w;
       w[0] = pack_bf16x2(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv);
       w[1] = pack_bf16x2(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
-      *reinterpret_cast<u32x2*>(Orow + b * 32 + 8 * g + 4 * half) = w;
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, qrow * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
-  if (half == 0) LSE[size_t(bh) * N + qrow] = (m + log2_fast(lt)) * kLn2;
+  if (half == 0 && qrow < N) LSE[size_t(bh) * N + qrow] = (m + log2_fast(lt)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
