@@ -24,6 +24,11 @@ FLAGS = [
     "-munsafe-fp-atomics",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the backward's per-step S and dP accumulators feed
+    # VALU work directly, and with the AGPR form the register allocator parks
+    # the long-lived dK/dV accumulators in VGPRs and copies them back and
+    # forth every step (the forward kernels are unaffected)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-result",
 ]
 

@@ -10,78 +10,78 @@
 //   D_i = sum_k dO_ik O_ik (= sum_j P_ij dP_ij),  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three kernels on the caller's stream:
-//  1. bwd_pre: D = rowsum(dO * O) in fp32, and zeroes the fp32 dQ accumulator
-//     (a fill kernel rather than a memset, so the sequence is graph-safe);
-//  2. bwd_main: one workgroup per (b, h, 128-key block); each of its 4 waves
-//     owns 32 keys whose K and V fragments stay in VGPRs and whose dK^T and
-//     dV^T accumulate on chip.  The workgroup streams 32-query steps (causal:
-//     starting at the diagonal): Q and dO are staged in LDS both row-major and
-//     transposed; S = Q K^T and dP = dO V^T put one key per lane, so P and dS
-//     feed the dV^T and dK^T MFMAs straight from registers; dS is written to
-//     LDS once so that dQ = dS K can be formed across all 128 keys and added to
-//     the fp32 accumulator with one coalesced atomic per element;
-//  3. bwd_dq_convert: dQ = bf16(scale * accumulator).
+// Three kernels on the caller's stream, none of them with atomics:
+//  1. bwd_pre: D = rowsum(dO * O) and LSE in base-2 units, both fp32.
+//  2. bwd_dkdv: one workgroup per (b, h, 128-key block); each of its 4 waves
+//     owns 32 keys.  K and V of those keys stay in VGPRs as the B operands of
+//     S = Q K^T and dP = dO V^T, so each lane holds one key and the recomputed
+//     P and dS feed dV^T += dO^T P and dK^T += Q^T dS straight from registers;
+//     dK^T and dV^T accumulate on chip for the whole sweep.  The workgroup
+//     streams 64-query steps (causal: from the diagonal on).  Q, dO and the
+//     per-row LSE and D of step i+1 go from HBM straight into LDS (buffer
+//     loads with the LDS destination) while step i computes; Q and dO are
+//     stored row-major only, and the transposed operands Q^T and dO^T are read
+//     with ds_read_b64_tr_b16.
+//  3. bwd_dq: one workgroup per (b, h, 128-query block), laid out like the
+//     forward kernel: each wave owns 32 queries whose Q and dO fragments stay
+//     in VGPRs, K and V tiles of 64 keys stream through double-buffered LDS,
+//     S^T = K Q^T and dP^T = V dO^T put one query per lane, and
+//     dQ^T += K^T dS^T takes dS^T from registers and K^T from transposing LDS
+//     reads of the K tile; dQ accumulates on chip.
+// Computing dQ in its own query-major pass costs two more N x N x d products
+// (S and dP recomputed) than accumulating it across key blocks, but the
+// per-key-block partial sums would need one fp32 atomic add per element and
+// key block, and on this GPU those are performed at the memory side at a
+// rate that caps the whole backward well below the MFMA rate.
 #include "fa_common.h"
 #include "fa_validate.h"
 
 namespace fa {
 
-template <int D>
-struct BwdTile {
-  static constexpr int NW = 4;
-  static constexpr int NT = 64 * NW;
-  static constexpr int BKV = 32 * NW;  // keys per workgroup
-  static constexpr int BQ = 32;        // queries per step
-  static constexpr int KS = D / 16;    // 16-wide k steps over d
-  static constexpr int DB = D / 32;    // 32-column blocks over d
-  static constexpr int QK_BYTES = BQ * D * 2;      // one row-major or transposed Q/dO tile
-  static constexpr int DS_BYTES = BQ * BKV * 2;    // dS tile [query][key]
-  static constexpr int KT_BYTES = D * BKV * 2;     // K^T [d][key]
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_DO = OFF_Q + QK_BYTES;
-  static constexpr int OFF_QT = OFF_DO + QK_BYTES;
-  static constexpr int OFF_DOT = OFF_QT + QK_BYTES;
-  static constexpr int OFF_DS = OFF_DOT + QK_BYTES;
-  static constexpr int OFF_KT = OFF_DS + DS_BYTES;
-  static constexpr int OFF_LSE = OFF_KT + KT_BYTES;
-  static constexpr int OFF_DD = OFF_LSE + BQ * 4;
-  static constexpr int LDS = OFF_DD + BQ * 4;
-  static constexpr int PIECES = (BQ / 4) * (D / 8);   // (4 rows x 8 cols) pieces of one Q tile
-  static_assert(2 * PIECES <= NT, "one Q or dO piece per thread");
-};
+// Byte offset, inside a row-major tile with rows of 2*DD bytes swizzled by
+// tile_swz<DD>, of the 8 bytes this lane reads with ds_read_b64_tr_b16 so that
+// lane l ends up with column 32*b + l%32 of rows row0 + {4h+8r2+0..3}
+// (h = l/32): in its 16-lane group g (lane t) it addresses row
+// 4*(g/2) + 8*r2 + t/4, columns 32*b + 16*(g%2) + 4*(t%4) .. +3.
+template <int DD>
+__device__ __forceinline__ int tr_off(int b, int r2, int lane) {
+  const int g = lane >> 4, t = lane & 15;
+  const int row = 4 * (g >> 1) + 8 * r2 + (t >> 2);
+  const int col = 32 * b + 16 * (g & 1) + 4 * (t & 3);
+  return row * (2 * DD) + (((col >> 3) ^ tile_swz<DD>(row)) * 16) + (col & 7) * 2;
+}
 
-// LDS offsets ---------------------------------------------------------------
-// Row-major [32 rows][D] tile (Q or dO), 16-byte units swizzled by row.
-template <int D>
-__device__ __forceinline__ int rm_offset(int row, int unit) {
-  return row * (D * 2) + swz<D / 8>(row, unit) * 16;
+__device__ __forceinline__ bf16x8 tr_pair(const char* base, int off0, int off1) {
+  typedef __attribute__((address_space(3))) short4_t* lds_s4;
+  const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + off0)));
+  const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + off1)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-// Transposed [D][32 rows] tile: rows of 64 bytes (4 units).  Within each group
-// of 16 query rows the 4-row chunks are stored (0, 2 | 1, 3) so that one
-// 16-byte unit holds the 8 queries one lane feeds to one MFMA k step.
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int tr_offset(int dcol, int qc) {
-  const int g = qc >> 2, cc = qc & 3;
-  const int unit = 2 * g + (cc & 1);
-  return dcol * 64 + ((unit ^ swz4(dcol)) * 16) + (cc >> 1) * 8;
+
+// 4 bytes per lane from a buffer straight into LDS: lane l writes lds[4*l .. 4*l+3].
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voffset, 0, 0, 0);
+#endif
 }
-// K^T [D][128 keys], plain key order, rows of 256 bytes (16 units).
-__device__ __forceinline__ int kt_offset(int dcol, int key) {
-  return dcol * 256 + swz<16>(dcol, key >> 3) * 16 + (key & 7) * 2;
-}
-// dS [32 queries][128 keys], rows of 256 bytes.
-__device__ __forceinline__ int ds_offset(int q, int key) {
-  return q * 256 + swz<16>(q, key >> 3) * 16 + (key & 7) * 2;
+
+// Source byte offset of the 16 bytes that a direct load places at byte p of a
+// row-major tile with rows of 2*DD bytes: LDS unit (row, pu) holds logical
+// unit pu ^ tile_swz<DD>(row) of that row.
+template <int DD>
+__device__ __forceinline__ int swz_src(int p) {
+  constexpr int RS = 2 * DD;
+  const int row = p / RS, pu = (p % RS) / 16;
+  return row * RS + ((pu ^ tile_swz<DD>(row)) * 16);
 }
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O) and zero the dQ accumulator.  8 lanes per row.
+// 1. D = rowsum(dO * O) and LSE2 = LSE * log2(e).  8 lanes per row.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256)
-bwd_pre_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, float* __restrict__ Dv,
-               float* __restrict__ dq_acc, long long rows) {
+bwd_pre_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
+               float* __restrict__ Dv, float* __restrict__ lse2, long long rows) {
   constexpr int PER = D / 8;  // elements per lane
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gid >> 3;
@@ -97,84 +97,112 @@ bwd_pre_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, floa
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
     }
-    float* z = dq_acc + row * D + sub * PER;
-#pragma unroll
-    for (int u = 0; u < PER / 4; ++u) *reinterpret_cast<f32x4*>(z + 4 * u) = f32x4{};
   }
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
-  if (row < rows && sub == 0) Dv[row] = acc;
+  if (row < rows && sub == 0) {
+    Dv[row] = acc;
+    lse2[row] = LSE[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 2. main kernel
+// 2. dK, dV: key-block-major sweep over the queries
 // ---------------------------------------------------------------------------
+template <int D>
+struct DkdvTile {
+  static constexpr int NW = 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BKV = 32 * NW;          // keys per workgroup
+  static constexpr int BQ = 64;                // queries per step
+  static constexpr int QB = BQ / 32;           // 32-query blocks per step
+  static constexpr int KS = D / 16;            // 16-wide k steps over d
+  static constexpr int DB = D / 32;            // 32-column blocks over d
+  static constexpr int PS = BQ / 16;           // 16-query k steps of dV, dK
+  static constexpr int RS = D * 2;             // bytes per Q / dO row
+  static constexpr int QT = BQ * RS;           // bytes of one Q or dO tile
+  static constexpr int OFF_DO = QT;
+  static constexpr int OFF_LSE = 2 * QT;       // BQ floats of LSE*log2(e)
+  static constexpr int OFF_DD = 2 * QT + BQ * 4;  // BQ floats of D
+  static constexpr int STAGE = 2 * QT + 2 * BQ * 4;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LPW = QT / 1024 / NW;   // 1 KiB direct loads per wave per Q (or dO) tile
+  static_assert(QT % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
+};
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
-bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-                float* __restrict__ dq_acc, __bf16* __restrict__ dK, __bf16* __restrict__ dV,
-                int N, int Tk, float c /* scale*log2(e) */, float scale) {
-  using T = BwdTile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[T::LDS];
+bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
+                __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int Tk, float c /* scale*log2(e) */,
+                float scale) {
+  using T = DkdvTile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
+  const int l32 = lane & 31;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / Tk;
-  int jt = tile - bh * Tk;
-  if (CAUSAL) jt = Tk - 1 - jt;  // blocks with fewer query steps last
+  const int jt = tile - bh * Tk;  // causal: key block 0 has the most query steps and is dispatched first
   const int k0 = jt * T::BKV;
   const size_t head = size_t(bh) * N * D;
-  const __bf16* Qh = Q + head;
-  const __bf16* Kh = K + head;
-  const __bf16* Vh = V + head;
-  const __bf16* dOh = dO + head;
-  const float* LSEh = LSE + size_t(bh) * N;
-  const float* Dh = Dv + size_t(bh) * N;
-  float* dQh = dq_acc + head;
+  const int head_bytes = N * T::RS;
 
-  // K and V fragments of this wave's keys: B operands (k = d, n = key).
+  // K and V fragments of this wave's keys: B operands of S = Q K^T and
+  // dP = dO V^T (lane: key kw0 + l32, d = 16*st + 8*half .. +7).  Keys past N
+  // read as zero; their dK and dV rows are never stored.
   const int kw0 = k0 + wave * 32;
-  const int key = kw0 + (lane & 31);
+  const int key = kw0 + l32;
   bf16x8 kf[T::KS], vf[T::KS];
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head, head_bytes);
 #pragma unroll
-  for (int s = 0; s < T::KS; ++s) {
-    if (key < N) {
-      kf[s] = *reinterpret_cast<const bf16x8*>(Kh + size_t(key) * D + 16 * s + 8 * half);
-      vf[s] = *reinterpret_cast<const bf16x8*>(Vh + size_t(key) * D + 16 * s + 8 * half);
-    } else {
-      kf[s] = bf16x8{};
-      vf[s] = bf16x8{};
+    for (int s = 0; s < T::KS; ++s) {
+      const int off = key * T::RS + (16 * s + 8 * half) * 2;
+      kf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      vf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
   }
-  // K^T of the whole 128-key block into LDS (B operand of dQ = dS K).
-  {
-    char* kt = smem + T::OFF_KT;
-    constexpr int KT_PIECES = (T::BKV / 4) * (D / 8);
-    for (int p = tid; p < KT_PIECES; p += T::NT) {
-      const int dc = p % (D / 8), kc = p / (D / 8);
-      u32x4 r[4];
+
+  // Direct-to-LDS loads of the Q and dO tiles of a step: load u of this wave
+  // fills bytes [(wave*LPW + u) KiB, +1 KiB) of each tile.
+  int goff[T::LPW];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = k0 + kc * 4 + i;
-        r[i] = kk < N ? *reinterpret_cast<const u32x4*>(Kh + size_t(kk) * D + dc * 8) : u32x4{};
-      }
+  for (int u = 0; u < T::LPW; ++u) goff[u] = swz_src<D>((wave * T::LPW + u) * 1024 + 16 * lane);
+  const float* lse2h = LSE2 + size_t(bh) * N;
+  const float* dh = Dv + size_t(bh) * N;
+  auto issue_loads = [&](int i, int stage) {
+    const int q0 = i * T::BQ;
+    const int bytes = (N - q0) * T::RS;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head + size_t(q0) * D, bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dO + head + size_t(q0) * D, bytes);
+    char* dst = smem + stage * T::STAGE + wave * T::LPW * 1024;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x2 lo, hi;
-        lo[0] = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-        lo[1] = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-        hi[0] = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-        hi[1] = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-        const int dcol = dc * 8 + 2 * w;
-        *reinterpret_cast<u32x2*>(kt + kt_offset(dcol, kc * 4)) = lo;
-        *reinterpret_cast<u32x2*>(kt + kt_offset(dcol + 1, kc * 4)) = hi;
-      }
-    }
+    for (int u = 0; u < T::LPW; ++u) load_lds16(rq, dst + u * 1024, goff[u]);
+#pragma unroll
+    for (int u = 0; u < T::LPW; ++u) load_lds16(rd, dst + T::OFF_DO + u * 1024, goff[u]);
+    // Rows past N read as zero: with their Q and dO rows zero as well, P = 1
+    // and dS = 0 there, and dO = 0 removes them from dV.
+    if (wave == 0) load_lds4(make_rsrc(lse2h + q0, (N - q0) * 4), smem + stage * T::STAGE + T::OFF_LSE, 4 * lane);
+    if (wave == 1) load_lds4(make_rsrc(dh + q0, (N - q0) * 4), smem + stage * T::STAGE + T::OFF_DD, 4 * lane);
+  };
+
+  // LDS read offsets.
+  // Q / dO rows (A operand of S and dP): row 32*qb + l32, logical unit 2*st + half.
+  int rof[T::KS];
+#pragma unroll
+  for (int st = 0; st < T::KS; ++st) rof[st] = l32 * T::RS + (((2 * st + half) ^ tile_swz<D>(l32)) * 16);
+  // Q^T / dO^T (A operand of dK, dV), column block b.
+  int tof[T::DB][2];
+#pragma unroll
+  for (int b = 0; b < T::DB; ++b) {
+    tof[b][0] = tr_off<D>(b, 0, lane);
+    tof[b][1] = tr_off<D>(b, 1, lane);
   }
 
   f32x16 dkt[T::DB], dvt[T::DB];
@@ -185,135 +213,114 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
   }
 
   const int Tq = (N + T::BQ - 1) / T::BQ;
-  const int i_begin = CAUSAL ? (k0 / T::BQ) : 0;
+  const int i0 = CAUSAL ? k0 / T::BQ : 0;
 
-  // staging roles: threads [0, PIECES) load Q pieces, [PIECES, 2*PIECES) dO pieces
-  const bool stager = tid < 2 * T::PIECES;
-  const bool st_is_do = tid >= T::PIECES;
-  const int pidx = st_is_do ? tid - T::PIECES : tid;
-  const int st_dc = pidx % (D / 8), st_qc = pidx / (D / 8);
+  issue_loads(i0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
 
-  for (int i = i_begin; i < Tq; ++i) {
+  for (int i = i0; i < Tq; ++i) {
+    const int stage = (i - i0) & 1;
+    if (i + 1 < Tq) issue_loads(i + 1, stage ^ 1);
+    const char* sb = smem + stage * T::STAGE;
     const int qs = i * T::BQ;
-    // ---- stage Q_i, dO_i (row-major and transposed), LSE and D
-    if (stager) {
-      const __bf16* src = st_is_do ? dOh : Qh;
-      u32x4 r[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int qq = qs + st_qc * 4 + x;
-        r[x] = qq < N ? *reinterpret_cast<const u32x4*>(src + size_t(qq) * D + st_dc * 8) : u32x4{};
-      }
-      char* rm = smem + (st_is_do ? T::OFF_DO : T::OFF_Q);
-      char* tr = smem + (st_is_do ? T::OFF_DOT : T::OFF_QT);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) *reinterpret_cast<u32x4*>(rm + rm_offset<D>(st_qc * 4 + x, st_dc)) = r[x];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x2 lo, hi;
-        lo[0] = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-        lo[1] = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-        hi[0] = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-        hi[1] = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-        const int dcol = st_dc * 8 + 2 * w;
-        *reinterpret_cast<u32x2*>(tr + tr_offset(dcol, st_qc)) = lo;
-        *reinterpret_cast<u32x2*>(tr + tr_offset(dcol + 1, st_qc)) = hi;
-      }
-    }
-    if (tid < T::BQ) {
-      const int qq = qs + tid;
-      // rows past N get LSE = +inf, so their recomputed P is exactly 0
-      reinterpret_cast<float*>(smem + T::OFF_LSE)[tid] = qq < N ? LSEh[qq] * kLog2e : INFINITY;
-      reinterpret_cast<float*>(smem + T::OFF_DD)[tid] = qq < N ? Dh[qq] : 0.f;
-    }
-    __syncthreads();
 
-    // ---- per-wave recompute and dK, dV accumulation
-    // skip a wave whose keys all come after every query of this step
-    const bool wave_visible = !CAUSAL || (kw0 <= qs + T::BQ - 1);
-    char* dss = smem + T::OFF_DS;
-    if (wave_visible && kw0 < N) {
-      const char* qsm = smem + T::OFF_Q;
-      const char* dosm = smem + T::OFF_DO;
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    // ---- S = Q K^T and dP = dO V^T (lane: key; element j: query 32*qb + acc_row(j)).
+    // The A operands of k step st+1 are read while the MFMAs of step st run.
+    f32x16 sacc[T::QB], pacc[T::QB];
+#pragma unroll
+    for (int qb = 0; qb < T::QB; ++qb) {
+      sacc[qb] = f32x16{};
+      pacc[qb] = f32x16{};
+    }
+    {
+      bf16x8 qa[T::QB], da[T::QB];
+#pragma unroll
+      for (int qb = 0; qb < T::QB; ++qb) {
+        qa[qb] = *reinterpret_cast<const bf16x8*>(sb + qb * 32 * T::RS + rof[0]);
+        da[qb] = *reinterpret_cast<const bf16x8*>(sb + T::OFF_DO + qb * 32 * T::RS + rof[0]);
+      }
 #pragma unroll
       for (int st = 0; st < T::KS; ++st) {
-        const int row = lane & 31;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qsm + rm_offset<D>(row, 2 * st + half));
-        sacc = mfma32(qa, kf[st], sacc);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(dosm + rm_offset<D>(row, 2 * st + half));
-        dpacc = mfma32(da, vf[st], dpacc);
+        bf16x8 qn[T::QB], dn[T::QB];
+        if (st + 1 < T::KS) {
+#pragma unroll
+          for (int qb = 0; qb < T::QB; ++qb) {
+            qn[qb] = *reinterpret_cast<const bf16x8*>(sb + qb * 32 * T::RS + rof[st + 1]);
+            dn[qb] = *reinterpret_cast<const bf16x8*>(sb + T::OFF_DO + qb * 32 * T::RS + rof[st + 1]);
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < T::QB; ++qb) {
+          sacc[qb] = mfma32(qa[qb], kf[st], sacc[qb]);
+          pacc[qb] = mfma32(da[qb], vf[st], pacc[qb]);
+        }
+        if (st + 1 < T::KS) {
+#pragma unroll
+          for (int qb = 0; qb < T::QB; ++qb) {
+            qa[qb] = qn[qb];
+            da[qb] = dn[qb];
+          }
+        }
       }
-      // lane holds key `key`; element j is query qs + acc_row(j)
-      const float* lse2 = reinterpret_cast<const float*>(smem + T::OFF_LSE);
-      const float* dd = reinterpret_cast<const float*>(smem + T::OFF_DD);
-      bf16x8 pb[2], dsb[2];
+    }
+
+    // ---- P = exp2(S*c - LSE2) and dS = P * (dP - D), rounded to bf16
+    bf16x8 pb[T::PS], db[T::PS];
+#pragma unroll
+    for (int qb = 0; qb < T::QB; ++qb) {
+      // causal: keys after the query are masked; only blocks that straddle the diagonal need it
+      const bool need = CAUSAL && (qs + qb * 32 < kw0 + 31);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * g + 4 * half);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + 8 * g + 4 * half);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sb + T::OFF_LSE + (qb * 32 + 8 * g + 4 * half) * 4);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sb + T::OFF_DD + (qb * 32 + 8 * g + 4 * half) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * g + e;
-          const int qq = qs + 8 * g + 4 * half + e;
-          float p = exp2_fast(fmaf(sacc[j], c, -l4[e]));
-          if (key >= N || (CAUSAL && key > qq)) p = 0.f;
-          const float ds = p * (dpacc[j] - d4[e]);
-          pb[j >> 3][j & 7] = (__bf16)p;
-          const __bf16 dsh = (__bf16)ds;
-          dsb[j >> 3][j & 7] = dsh;
-          *reinterpret_cast<__bf16*>(dss + ds_offset(8 * g + 4 * half + e, wave * 32 + (lane & 31))) = dsh;
+          float p = exp2_fast(fmaf(sacc[qb][j], c, -l4[e]));
+          if (need && key > qs + qb * 32 + 8 * g + 4 * half + e) p = 0.f;
+          const float ds = p * (pacc[qb][j] - d4[e]);
+          pb[qb * 2 + (j >> 3)][j & 7] = (__bf16)p;
+          db[qb * 2 + (j >> 3)][j & 7] = (__bf16)ds;
         }
       }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (k = query)
-      const char* qt = smem + T::OFF_QT;
-      const char* dot = smem + T::OFF_DOT;
-#pragma unroll
-      for (int b = 0; b < T::DB; ++b) {
-        const int dcol = b * 32 + (lane & 31);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int off = dcol * 64 + (((2 * h + half) ^ swz4(dcol)) * 16);
-          const bf16x8 doa = *reinterpret_cast<const bf16x8*>(dot + off);
-          dvt[b] = mfma32(doa, pb[h], dvt[b]);
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + off);
-          dkt[b] = mfma32(qa, dsb[h], dkt[b]);
-        }
-      }
-    } else {
-      // this wave's keys contribute nothing to the step: zero its dS columns
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        *reinterpret_cast<__bf16*>(dss + ds_offset(acc_row(j, lane), wave * 32 + (lane & 31))) = (__bf16)0.f;
     }
-    __syncthreads();
 
-    // ---- dQ_i += dS K over the 128 keys: wave w owns column block w
-    if (wave < T::DB) {
-      const char* kt = smem + T::OFF_KT;
-      f32x16 acc = f32x16{};
-      const int row = lane & 31;
-      const int dcol = wave * 32 + (lane & 31);
+    // ---- dV^T += dO^T P,  dK^T += Q^T dS  (k = query, in the accumulator's order);
+    // the transposed operands of the next (ps, b) are read one MFMA pair ahead
+    {
+      bf16x8 doa = tr_pair(sb + T::OFF_DO, tof[0][0], tof[0][1]);
+      bf16x8 qta = tr_pair(sb, tof[0][0], tof[0][1]);
 #pragma unroll
-      for (int ks = 0; ks < T::BKV / 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(dss + row * 256 + swz<16>(row, 2 * ks + half) * 16);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(kt + dcol * 256 + swz<16>(dcol, 2 * ks + half) * 16);
-        acc = mfma32(a, b, acc);
-      }
-      // element j: query qs + acc_row(j), column dcol
+      for (int ps = 0; ps < T::PS; ++ps)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qq = qs + acc_row(j, lane);
-        if (qq < N) unsafeAtomicAdd(dQh + size_t(qq) * D + dcol, acc[j]);
-      }
+        for (int b = 0; b < T::DB; ++b) {
+          const int nb = (b + 1 < T::DB) ? b + 1 : 0;
+          const int nps = (b + 1 < T::DB) ? ps : ps + 1;
+          bf16x8 don, qtn;
+          if (nps < T::PS) {
+            don = tr_pair(sb + T::OFF_DO + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
+            qtn = tr_pair(sb + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
+          }
+          dvt[b] = mfma32(doa, pb[ps], dvt[b]);
+          dkt[b] = mfma32(qta, db[ps], dkt[b]);
+          if (nps < T::PS) {
+            doa = don;
+            qta = qtn;
+          }
+        }
     }
+
+    // the loads of step i+1 have landed; every wave is done with this stage
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
-  // ---- epilogue: dK = scale * dK^T^T, dV = dV^T^T; lane holds key `key`
-  if (key >= N) return;
-  __bf16* dKr = dK + head + size_t(key) * D;
-  __bf16* dVr = dV + head + size_t(key) * D;
+  // ---- epilogue: dK = scale * (dK^T)^T, dV = (dV^T)^T; lane holds key `key`,
+  // keys past N are dropped by the buffer bounds
+  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(dK + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(dV + head, head_bytes);
 #pragma unroll
   for (int b = 0; b < T::DB; ++b)
 #pragma unroll
@@ -324,26 +331,211 @@ bwd_main_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
       wk[1] = pack_bf16x2(dkt[b][4 * g + 2] * scale, dkt[b][4 * g + 3] * scale);
       wv[0] = pack_bf16x2(dvt[b][4 * g + 0], dvt[b][4 * g + 1]);
       wv[1] = pack_bf16x2(dvt[b][4 * g + 2], dvt[b][4 * g + 3]);
-      *reinterpret_cast<u32x2*>(dKr + col) = wk;
-      *reinterpret_cast<u32x2*>(dVr + col) = wv;
+      __builtin_amdgcn_raw_buffer_store_b64(wk, rdk, key * T::RS + col * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(wv, rdv, key * T::RS + col * 2, 0, 0);
     }
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ = bf16(scale * accumulator), 8 elements per thread
+// 3. dQ: query-block-major sweep over the keys
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-bwd_dq_convert_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq, long long n8, float scale) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(acc + 8 * i);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(acc + 8 * i + 4);
-  u32x4 w;
-  w[0] = pack_bf16x2(a[0] * scale, a[1] * scale);
-  w[1] = pack_bf16x2(a[2] * scale, a[3] * scale);
-  w[2] = pack_bf16x2(b[0] * scale, b[1] * scale);
-  w[3] = pack_bf16x2(b[2] * scale, b[3] * scale);
-  *reinterpret_cast<u32x4*>(dq + 8 * i) = w;
+template <int D>
+struct DqTile {
+  static constexpr int NW = 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 32 * NW;              // queries per workgroup
+  static constexpr int BC = 64;                   // keys per tile
+  static constexpr int KS = D / 16;               // 16-wide k steps over d
+  static constexpr int DB = D / 32;               // 32-column blocks of dQ
+  static constexpr int KB = BC / 32;              // 32-key blocks of S^T
+  static constexpr int PS = BC / 16;              // 16-key k steps of dQ^T
+  static constexpr int RS = D * 2;                // bytes per K or V row
+  static constexpr int TILE = BC * RS;            // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;          // K tile then V tile
+  static constexpr int LPW = TILE / 1024 / NW;
+  static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2)
+bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+              const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
+              __bf16* __restrict__ dQ, int N, int Tr, float c /* scale*log2(e) */, float scale) {
+  using T = DqTile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / Tr;
+  int it = tile - bh * Tr;
+  if (CAUSAL) it = Tr - 1 - it;  // longest rows first
+  const int q0 = it * T::BR;
+  const size_t head = size_t(bh) * N * D;
+  const __bf16* Kh = K + head;
+  const __bf16* Vh = V + head;
+  const int head_bytes = N * T::RS;
+
+  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): row
+  // qrow, columns 16*s + 8*half .. +7.  Rows past N read as zero.
+  const int wq0 = q0 + wave * 32;
+  const int qrow = wq0 + l32;
+  bf16x8 qf[T::KS], df[T::KS];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dO + head, head_bytes);
+#pragma unroll
+    for (int s = 0; s < T::KS; ++s) {
+      const int off = qrow * T::RS + (16 * s + 8 * half) * 2;
+      qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      df[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
+    }
+  }
+  // this lane's query: LSE in base 2 and D (rows past N: 0; their dQ is never stored)
+  float lq = 0.f, dd = 0.f;
+  if (qrow < N) {
+    lq = LSE2[size_t(bh) * N + qrow];
+    dd = Dv[size_t(bh) * N + qrow];
+  }
+
+  const int Tc = (N + T::BC - 1) / T::BC;
+  int nt = Tc;
+  if (CAUSAL) nt = min(Tc, (min(q0 + T::BR, N) - 1) / T::BC + 1);
+  const bool wave_active = wq0 < N;
+  int nt_w = nt;
+  if (CAUSAL && wave_active) nt_w = min(nt, (min(wq0 + 32, N) - 1) / T::BC + 1);
+
+  int goff[T::LPW];
+#pragma unroll
+  for (int u = 0; u < T::LPW; ++u) goff[u] = swz_src<D>((wave * T::LPW + u) * 1024 + 16 * lane);
+  auto issue_loads = [&](int j, int stage) {
+    const int key0 = j * T::BC;
+    const int bytes = (N - key0) * T::RS;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + size_t(key0) * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + size_t(key0) * D, bytes);
+    char* dst = smem + stage * T::STAGE + wave * T::LPW * 1024;
+#pragma unroll
+    for (int u = 0; u < T::LPW; ++u) load_lds16(rk, dst + u * 1024, goff[u]);
+#pragma unroll
+    for (int u = 0; u < T::LPW; ++u) load_lds16(rv, dst + T::TILE + u * 1024, goff[u]);
+  };
+
+  // K / V rows (A operands of S^T and dP^T): rows kb*32 + l32, logical unit 2*st + half.
+  int rof[T::KS];
+#pragma unroll
+  for (int st = 0; st < T::KS; ++st) rof[st] = l32 * T::RS + (((2 * st + half) ^ tile_swz<D>(l32)) * 16);
+  // K^T (A operand of dQ^T), column block b.
+  int tof[T::DB][2];
+#pragma unroll
+  for (int b = 0; b < T::DB; ++b) {
+    tof[b][0] = tr_off<D>(b, 0, lane);
+    tof[b][1] = tr_off<D>(b, 1, lane);
+  }
+
+  f32x16 acc[T::DB];
+#pragma unroll
+  for (int b = 0; b < T::DB; ++b) acc[b] = f32x16{};
+
+  auto compute = [&](int j, const char* base) {
+    // ---- S^T = K_j Q^T and dP^T = V_j dO^T (lane: query; element r: key kb*32 + acc_row(r))
+    f32x16 s[T::KB], p[T::KB];
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+      s[kb] = f32x16{};
+      p[kb] = f32x16{};
+    }
+    {
+      bf16x8 ka[T::KB], va[T::KB];
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+        ka[kb] = *reinterpret_cast<const bf16x8*>(base + kb * 32 * T::RS + rof[0]);
+        va[kb] = *reinterpret_cast<const bf16x8*>(base + T::TILE + kb * 32 * T::RS + rof[0]);
+      }
+#pragma unroll
+      for (int st = 0; st < T::KS; ++st) {
+        bf16x8 kn[T::KB], vn[T::KB];
+        if (st + 1 < T::KS) {
+#pragma unroll
+          for (int kb = 0; kb < T::KB; ++kb) {
+            kn[kb] = *reinterpret_cast<const bf16x8*>(base + kb * 32 * T::RS + rof[st + 1]);
+            vn[kb] = *reinterpret_cast<const bf16x8*>(base + T::TILE + kb * 32 * T::RS + rof[st + 1]);
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) {
+          s[kb] = mfma32(ka[kb], qf[st], s[kb]);
+          p[kb] = mfma32(va[kb], df[st], p[kb]);
+        }
+        if (st + 1 < T::KS) {
+#pragma unroll
+          for (int kb = 0; kb < T::KB; ++kb) {
+            ka[kb] = kn[kb];
+            va[kb] = vn[kb];
+          }
+        }
+      }
+    }
+    // ---- dS^T = P^T * (dP^T - D) with P^T = exp2(S^T*c - LSE2), rounded to bf16.
+    // Keys past N have zero K and V rows, so they add nothing to dQ; causal
+    // keys after the query are masked on the tiles that straddle the diagonal.
+    const int key0 = j * T::BC;
+    const bool need = CAUSAL && (key0 + T::BC - 1 > wq0);
+    bf16x8 db[T::PS];
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = exp2_fast(fmaf(s[kb][r], c, -lq));
+        if (need && key0 + kb * 32 + acc_row(r, lane) > qrow) pr = 0.f;
+        db[kb * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (p[kb][r] - dd));
+      }
+    // ---- dQ^T += K_j^T dS^T (k = key, in the accumulator's order)
+    bf16x8 ka = tr_pair(base, tof[0][0], tof[0][1]);
+#pragma unroll
+    for (int ps = 0; ps < T::PS; ++ps)
+#pragma unroll
+      for (int b = 0; b < T::DB; ++b) {
+        const int nb = (b + 1 < T::DB) ? b + 1 : 0;
+        const int nps = (b + 1 < T::DB) ? ps : ps + 1;
+        bf16x8 kn;
+        if (nps < T::PS) kn = tr_pair(base + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
+        acc[b] = mfma32(ka, db[ps], acc[b]);
+        if (nps < T::PS) ka = kn;
+      }
+  };
+
+  auto step = [&](int j, int stage) {
+    if (j + 1 < nt) issue_loads(j + 1, stage ^ 1);
+    if (wave_active && j < nt_w) compute(j, smem + stage * T::STAGE);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j+1 have landed
+    __syncthreads();
+  };
+
+  issue_loads(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < nt; j += 2) {
+    step(j, 0);
+    step(j + 1, 1);
+  }
+  if (j < nt) step(j, 0);
+
+  if (!wave_active) return;
+  // dQ = scale * (dQ^T)^T; lane holds query qrow, rows past N are dropped by the buffer bounds
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(dQ + head, head_bytes);
+#pragma unroll
+  for (int b = 0; b < T::DB; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[b][4 * g + 0] * scale, acc[b][4 * g + 1] * scale);
+      w[1] = pack_bf16x2(acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, qrow * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -353,30 +545,32 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
                                void* ws, hipStream_t st) {
-  using T = BwdTile<D>;
   const long long rows = (long long)B * H * N;
-  const size_t acc_bytes = (size_t(rows) * D * 4 + 255) / 256 * 256;
-  float* dq_acc = reinterpret_cast<float*>(ws);
-  float* Dv = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + acc_bytes);
+  const BwdWorkspace w = bwd_workspace_layout(Shape{B, H, N, D});
+  char* base = reinterpret_cast<char*>(ws);
+  float* Dv = reinterpret_cast<float*>(base + w.d);
+  float* lse2 = reinterpret_cast<float*>(base + w.lse2);
+  const float c = scale * kLog2e;
 
   const long long pre_blocks = (rows * 8 + 255) / 256;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, st,
-                     (const __bf16*)o, (const __bf16*)dO, Dv, dq_acc, rows);
+                     (const __bf16*)o, (const __bf16*)dO, lse, Dv, lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int Tk = (N + T::BKV - 1) / T::BKV;
-  const long long G = (long long)B * H * Tk;
-  if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(T::NT), 0, st,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO, lse, Dv, dq_acc,
-                     (__bf16*)dk, (__bf16*)dv, N, Tk, scale * kLog2e, scale);
+  const int Tk = (N + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV;
+  const long long Gk = (long long)B * H * Tk;
+  const int Tr = (N + DqTile<D>::BR - 1) / DqTile<D>::BR;
+  const long long Gq = (long long)B * H * Tr;
+  if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
+                     (const float*)lse2, (const float*)Dv, (__bf16*)dk, (__bf16*)dv, N, Tk, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-
-  const long long n8 = rows * D / 8;
-  hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
-                     (const float*)dq_acc, (__bf16*)dq, n8, scale);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)Gq), dim3(DqTile<D>::NT), 0, st,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
+                     (const float*)lse2, (const float*)Dv, (__bf16*)dq, N, Tr, c, scale);
   return hipGetLastError();
 }
 

@@ -24,10 +24,14 @@ struct Shape {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Elements per [B][H][N][d] tensor, or -1 if the shape is invalid / too large.
+// Besides the 2^31 elements per tensor, one head's fp32 slab plus 256 rows of
+// slack must stay below 2^31 bytes: the kernels address a head with 32-bit
+// byte offsets, including rows just past N that the buffer bounds discard.
 inline int64_t tensor_elems(const Shape& s) {
   if (s.B < 1 || s.H < 1 || s.N < 1 || s.d < 1) return -1;
   const int64_t n = int64_t(s.B) * s.H * s.N * s.d;
   if (n >= (int64_t(1) << 31)) return -1;
+  if ((int64_t(s.N) + 256) * s.d * 4 >= (int64_t(1) << 31)) return -1;
   return n;
 }
 
@@ -62,14 +66,26 @@ inline int validate_fwd(const void* q, const void* k, const void* v, const void*
   return kOk;
 }
 
-// Workspace of the backward: fp32 dQ accumulator, then fp32 D row terms,
-// each rounded up to 256 bytes.
-inline size_t bwd_workspace_bytes(const Shape& s) {
+// Workspace of the backward, in this order, each part rounded up to 256
+// bytes: the fp32 row terms D = rowsum(dO * O) [B][H][N] and the fp32 LSE in
+// base-2 units [B][H][N].
+struct BwdWorkspace {
+  size_t d, lse2, total;
+};
+
+inline BwdWorkspace bwd_workspace_layout(const Shape& s) {
   const int64_t n = tensor_elems(s);
-  if (n < 0 || (s.d != 64 && s.d != 128)) return 0;
+  if (n < 0 || (s.d != 64 && s.d != 128)) return BwdWorkspace{0, 0, 0};
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  return up(size_t(n) * 4) + up(size_t(s.B) * s.H * s.N * 4);
+  const size_t rows = size_t(s.B) * s.H * s.N;
+  BwdWorkspace w;
+  w.d = 0;
+  w.lse2 = up(rows * 4);
+  w.total = w.lse2 + up(rows * 4);
+  return w;
 }
+
+inline size_t bwd_workspace_bytes(const Shape& s) { return bwd_workspace_layout(s).total; }
 
 inline int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
                         const void* dO, const void* dq, const void* dk, const void* dv,
@@ -103,7 +119,7 @@ inline const char* status_string(int st) {
   switch (st) {
     case kOk: return "FA_OK: success";
     case kErrNull: return "FA_ERR_NULL: a required pointer is NULL";
-    case kErrShape: return "FA_ERR_SHAPE: B, H and N must be >= 1 and each tensor < 2^31 elements";
+    case kErrShape: return "FA_ERR_SHAPE: B, H and N must be >= 1, each tensor < 2^31 elements and (N+256)*d*4 < 2^31";
     case kErrHeadDim: return "FA_ERR_HEAD_DIM: head dimension d must be 64 or 128";
     case kErrScale: return "FA_ERR_SCALE: scale must be finite and > 0";
     case kErrAlign: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";

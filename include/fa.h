@@ -25,7 +25,9 @@
  *   mutable global state, never synchronises and never prints; calls are
  *   re-entrant and thread-safe.
  * Preconditions: B, H, N >= 1; d in {64, 128}; causal in {0, 1};
- *   scale finite and > 0; B*H*N*d < 2^31 elements per tensor.
+ *   scale finite and > 0; B*H*N*d < 2^31 elements per tensor and
+ *   (N + 256)*d*4 < 2^31 (one head's fp32 slab is addressed with 32-bit
+ *   byte offsets).
  * Causal mask: key j is visible to query i iff j <= i (queries and keys have
  *   the same length N).
  * Log-sum-exp: lse[b][h][i] = ln( sum over visible j of exp(scale * q_i . k_j) ),
@@ -50,7 +52,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL */
-  FA_ERR_SHAPE = -2,     /* B, H or N < 1, or a tensor too large for 32-bit element counts */
+  FA_ERR_SHAPE = -2,     /* B, H or N < 1, or a tensor or head too large for 32-bit offsets */
   FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 */
   FA_ERR_SCALE = -4,     /* scale not finite or not > 0 */
   FA_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
@@ -85,9 +87,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 /*
  * fa_bwd_workspace_bytes - size in bytes of the workspace fa_bwd needs for
- * these sizes: an fp32 dQ accumulator [B][H][N][d] plus the fp32 row terms
- * D = rowsum(dO * O) [B][H][N] (both padded).  Returns 0 if the sizes are
- * invalid.
+ * these sizes: the fp32 row terms D = rowsum(dO * O) [B][H][N] and the fp32
+ * LSE in base-2 units [B][H][N] (each padded to 256 bytes).  Returns 0 if
+ * the sizes are invalid.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -99,8 +101,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  * workspace: device buffer of at least fa_bwd_workspace_bytes(B,H,N,d) bytes,
  * owned by the caller; its contents on entry do not matter and are
  * clobbered.  P is recomputed tile by tile from q, k and lse; the N x N
- * matrices are never written to memory.  dQ is accumulated in fp32 with
- * atomic adds, so its low bits may differ from run to run.
+ * matrices are never written to memory.  dK and dV are accumulated in a
+ * key-block-major pass and dQ in a query-block-major pass, both in fp32 on
+ * chip without atomics, so the results are bitwise reproducible.
  * Defined by: FlashAttention-from-GPU-memory page, section 2.2
  * (recomputation); FlashAttention optimisation page, section 4.2 (backward
  * tiled like the forward); the gradients are the chain rule on the forward.

@@ -85,6 +85,7 @@ def test_fwd_validation(lib, fn):
     assert f(q, k, v, o, l, 1, -1, 8, 64, 0.125, 0, None) == ST["SHAPE"]
     assert f(q, k, v, o, l, 1, 1, 0, 64, 0.125, 0, None) == ST["SHAPE"]
     assert f(q, k, v, o, l, 1 << 12, 1 << 10, 1 << 10, 64, 0.125, 0, None) == ST["SHAPE"]
+    assert f(q, k, v, o, l, 1, 1, (1 << 22) - 256, 128, 0.125, 0, None) == ST["SHAPE"]  # one head > 2^31 B fp32
     assert f(q, k, v, o, l, 1, 1, 8, 96, 0.125, 0, None) == ST["HEAD_DIM"]
     assert f(q, k, v, o, l, 1, 1, 8, 256, 0.125, 0, None) == ST["HEAD_DIM"]
     assert f(q, k, v, o, l, 1, 1, 8, 64, float("nan"), 0, None) == ST["SCALE"]
@@ -100,7 +101,7 @@ def test_fwd_validation(lib, fn):
 
 def test_bwd_workspace_bytes(lib):
     n = 2 * 3 * 100 * 128
-    want = (n * 4 + 255) // 256 * 256 + (2 * 3 * 100 * 4 + 255) // 256 * 256
+    want = 2 * ((2 * 3 * 100 * 4 + 255) // 256 * 256)
     assert lib.fa_bwd_workspace_bytes(2, 3, 100, 128) == want
     assert lib.fa_bwd_workspace_bytes(0, 3, 100, 128) == 0
     assert lib.fa_bwd_workspace_bytes(1, 1, 100, 80) == 0
@@ -162,7 +163,10 @@ int main() {
   EXPECT(tensor_elems(Shape{1024, 1024, 1024, 2}) == -1);
   EXPECT(tensor_elems(Shape{2, 3, 5, 64}) == 1920);
   size_t need = bwd_workspace_bytes(s);
-  EXPECT(need == 8192 + 256);
+  EXPECT(need == 256 + 256);
+  EXPECT(bwd_workspace_layout(s).d == 0 && bwd_workspace_layout(s).lse2 == 256);
+  EXPECT(tensor_elems(Shape{1, 1, (1 << 22) - 256, 128}) == -1);
+  EXPECT(tensor_elems(Shape{1, 1, (1 << 22) - 257, 128}) > 0);
   EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s, 0.125f, 1,
                       ws, sizeof ws) == kOk);
   EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s, 0.125f, 1,

@@ -240,7 +240,8 @@ def test_full_size_backward_sampled_heads(gpu_lib, name, heads):
 
 
 def test_bwd_workspace_reuse_and_stale_contents(gpu_lib):
-    """A workspace holding garbage from an earlier, larger call gives the same result."""
+    """A workspace holding garbage from an earlier, larger call gives the same
+    result, bit for bit: the backward has no atomics, so it is deterministic."""
     q, k, v, do = _gpu(*make_inputs(1, 2, 700, 128, "bf16", seed=500, backward=True))
     ws = torch.full((gpu_lib.bwd_workspace_bytes(2, 4, 2000, 128),), 0x7f, dtype=torch.uint8, device="cuda")
     o, lse = gpu_lib.fwd(q, k, v, causal=True)
@@ -248,5 +249,4 @@ def test_bwd_workspace_reuse_and_stale_contents(gpu_lib):
     b = gpu_lib.bwd(q, k, v, o, lse, do, causal=True)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
-        assert (x.float() - y.float()).abs().max().item() <= 2e-2 * y.float().abs().max().item()
-    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])  # dK, dV have no atomics
+        assert torch.equal(x, y)
