@@ -12,16 +12,16 @@
 //
 // Three kernels on the caller's stream, none of them with atomics:
 //  1. bwd_pre: D = rowsum(dO * O) and LSE in base-2 units, both fp32.
-//  2. bwd_dkdv: one workgroup per (b, h, 128-key block); each of its 4 waves
-//     owns 32 keys.  K and V of those keys stay in VGPRs as the B operands of
-//     S = Q K^T and dP = dO V^T, so each lane holds one key and the recomputed
-//     P and dS feed dV^T += dO^T P and dK^T += Q^T dS straight from registers;
-//     dK^T and dV^T accumulate on chip for the whole sweep.  The workgroup
-//     streams 64-query steps (causal: from the diagonal on).  Q, dO and the
-//     per-row LSE and D of step i+1 go from HBM straight into LDS (buffer
-//     loads with the LDS destination) while step i computes; Q and dO are
-//     stored row-major only, and the transposed operands Q^T and dO^T are read
-//     with ds_read_b64_tr_b16.
+//  2. bwd_dkdv: one workgroup per (b, h, 128-key block), eight waves in four
+//     pairs of 32 keys.  K (or V) of those keys stays in VGPRs as the B
+//     operand of S = Q K^T (or dP = dO V^T), so each lane holds one key and
+//     the recomputed P (or dS) feeds dV^T += dO^T P (or dK^T += Q^T dS)
+//     straight from registers; dK^T and dV^T accumulate on chip for the whole
+//     sweep.  The workgroup streams 64-query steps (causal: from the diagonal
+//     on).  Q, dO and the per-row LSE and D of step i+1 go from HBM straight
+//     into LDS (buffer loads with the LDS destination) while step i computes;
+//     Q and dO are stored row-major only, and the transposed operands Q^T and
+//     dO^T are read with ds_read_b64_tr_b16.
 //  3. bwd_dq: one workgroup per (b, h, 128-query block), laid out like the
 //     forward kernel: each wave owns 32 queries whose Q and dO fragments stay
 //     in VGPRs, K and V tiles of 64 keys stream through double-buffered LDS,
@@ -108,13 +108,24 @@ bwd_pre_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, cons
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV: key-block-major sweep over the queries
+// 2. dK, dV: key-block-major sweep over the queries.
+//
+// Eight waves per workgroup, two per SIMD, in pairs that share 32 keys:
+//  * wave A (waves 0-3) holds K of its keys, forms S = Q K^T and
+//    P = exp2(S*c - LSE2), hands P to its partner through LDS and
+//    accumulates dV^T += dO^T P;
+//  * wave B (waves 4-7) holds V of the same keys, forms dP = dO V^T, reads P
+//    back and forms dS = P * (dP - D), and accumulates dK^T += Q^T dS.
+// Both roles run the same two products on different operands (Q and K vs dO
+// and V, then dO^T vs Q^T), so one wave's MFMAs overlap the other's VALU work
+// on the same SIMD, and each wave needs only one K/V fragment set and one
+// accumulator set.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvTile {
-  static constexpr int NW = 4;
+  static constexpr int NW = 8;
   static constexpr int NT = 64 * NW;
-  static constexpr int BKV = 32 * NW;          // keys per workgroup
+  static constexpr int BKV = 128;              // keys per workgroup, 32 per wave pair
   static constexpr int BQ = 64;                // queries per step
   static constexpr int QB = BQ / 32;           // 32-query blocks per step
   static constexpr int KS = D / 16;            // 16-wide k steps over d
@@ -126,13 +137,15 @@ struct DkdvTile {
   static constexpr int OFF_LSE = 2 * QT;       // BQ floats of LSE*log2(e)
   static constexpr int OFF_DD = 2 * QT + BQ * 4;  // BQ floats of D
   static constexpr int STAGE = 2 * QT + 2 * BQ * 4;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int XP = 4 * QB * 4 * 64 * 16;  // P hand-over: 4 pairs x (QB*4 chunks of 16 B) x 64 lanes
+  static constexpr int OFF_XP = 2 * STAGE;
+  static constexpr int LDS = OFF_XP + XP;
   static constexpr int LPW = QT / 1024 / NW;   // 1 KiB direct loads per wave per Q (or dO) tile
   static_assert(QT % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(512, 1)
 bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                 const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
                 __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int Tk, float c /* scale*log2(e) */,
@@ -143,6 +156,8 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool role_a = wave < 4;  // wave-uniform
+  const int pair = wave & 3;
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -152,21 +167,17 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
   const size_t head = size_t(bh) * N * D;
   const int head_bytes = N * T::RS;
 
-  // K and V fragments of this wave's keys: B operands of S = Q K^T and
-  // dP = dO V^T (lane: key kw0 + l32, d = 16*st + 8*half .. +7).  Keys past N
-  // read as zero; their dK and dV rows are never stored.
-  const int kw0 = k0 + wave * 32;
+  // Fragments of this pair's keys: K (wave A) or V (wave B), the B operand of
+  // S = Q K^T or dP = dO V^T (lane: key kw0 + l32, d = 16*st + 8*half .. +7).
+  // Keys past N read as zero; their dK and dV rows are never stored.
+  const int kw0 = k0 + pair * 32;
   const int key = kw0 + l32;
-  bf16x8 kf[T::KS], vf[T::KS];
+  bf16x8 kv[T::KS];
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((role_a ? K : V) + head, head_bytes);
 #pragma unroll
-    for (int s = 0; s < T::KS; ++s) {
-      const int off = key * T::RS + (16 * s + 8 * half) * 2;
-      kf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-    }
+    for (int st = 0; st < T::KS; ++st)
+      kv[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, key * T::RS + (16 * st + 8 * half) * 2, 0, 0));
   }
 
   // Direct-to-LDS loads of the Q and dO tiles of a step: load u of this wave
@@ -192,25 +203,26 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     if (wave == 1) load_lds4(make_rsrc(dh + q0, (N - q0) * 4), smem + stage * T::STAGE + T::OFF_DD, 4 * lane);
   };
 
-  // LDS read offsets.
-  // Q / dO rows (A operand of S and dP): row 32*qb + l32, logical unit 2*st + half.
+  // Operand tiles of the two products: rows of Q (A) or dO (B) for the first,
+  // transposed dO (A) or Q (B) for the second.
+  const int off_rows = role_a ? 0 : T::OFF_DO;
+  const int off_tr = role_a ? T::OFF_DO : 0;
   int rof[T::KS];
 #pragma unroll
-  for (int st = 0; st < T::KS; ++st) rof[st] = l32 * T::RS + (((2 * st + half) ^ tile_swz<D>(l32)) * 16);
-  // Q^T / dO^T (A operand of dK, dV), column block b.
+  for (int st = 0; st < T::KS; ++st) rof[st] = off_rows + l32 * T::RS + (((2 * st + half) ^ tile_swz<D>(l32)) * 16);
   int tof[T::DB][2];
 #pragma unroll
   for (int b = 0; b < T::DB; ++b) {
-    tof[b][0] = tr_off<D>(b, 0, lane);
-    tof[b][1] = tr_off<D>(b, 1, lane);
+    tof[b][0] = off_tr + tr_off<D>(b, 0, lane);
+    tof[b][1] = off_tr + tr_off<D>(b, 1, lane);
   }
+  // P hand-over: lane `lane` of pair `pair` exchanges 16-byte chunk ch at
+  // OFF_XP + ((pair * QB*4 + ch) * 64 + lane) * 16.
+  char* xp = smem + T::OFF_XP + (pair * T::QB * 4 * 64 + lane) * 16;
 
-  f32x16 dkt[T::DB], dvt[T::DB];
+  f32x16 acc2[T::DB];  // dV^T (A) or dK^T (B)
 #pragma unroll
-  for (int b = 0; b < T::DB; ++b) {
-    dkt[b] = f32x16{};
-    dvt[b] = f32x16{};
-  }
+  for (int b = 0; b < T::DB; ++b) acc2[b] = f32x16{};
 
   const int Tq = (N + T::BQ - 1) / T::BQ;
   const int i0 = CAUSAL ? k0 / T::BQ : 0;
@@ -225,114 +237,107 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     const char* sb = smem + stage * T::STAGE;
     const int qs = i * T::BQ;
 
-    // ---- S = Q K^T and dP = dO V^T (lane: key; element j: query 32*qb + acc_row(j)).
-    // The A operands of k step st+1 are read while the MFMAs of step st run.
-    f32x16 sacc[T::QB], pacc[T::QB];
+    // ---- first product: S = Q K^T (A) or dP = dO V^T (B); lane: key,
+    // element j: query 32*qb + acc_row(j).  A operands read one k step ahead.
+    f32x16 acc1[T::QB];
 #pragma unroll
-    for (int qb = 0; qb < T::QB; ++qb) {
-      sacc[qb] = f32x16{};
-      pacc[qb] = f32x16{};
-    }
+    for (int qb = 0; qb < T::QB; ++qb) acc1[qb] = f32x16{};
     {
-      bf16x8 qa[T::QB], da[T::QB];
+      bf16x8 a[T::QB];
 #pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb) {
-        qa[qb] = *reinterpret_cast<const bf16x8*>(sb + qb * 32 * T::RS + rof[0]);
-        da[qb] = *reinterpret_cast<const bf16x8*>(sb + T::OFF_DO + qb * 32 * T::RS + rof[0]);
-      }
+      for (int qb = 0; qb < T::QB; ++qb) a[qb] = *reinterpret_cast<const bf16x8*>(sb + qb * 32 * T::RS + rof[0]);
 #pragma unroll
       for (int st = 0; st < T::KS; ++st) {
-        bf16x8 qn[T::QB], dn[T::QB];
+        bf16x8 an[T::QB];
         if (st + 1 < T::KS) {
 #pragma unroll
-          for (int qb = 0; qb < T::QB; ++qb) {
-            qn[qb] = *reinterpret_cast<const bf16x8*>(sb + qb * 32 * T::RS + rof[st + 1]);
-            dn[qb] = *reinterpret_cast<const bf16x8*>(sb + T::OFF_DO + qb * 32 * T::RS + rof[st + 1]);
-          }
+          for (int qb = 0; qb < T::QB; ++qb)
+            an[qb] = *reinterpret_cast<const bf16x8*>(sb + qb * 32 * T::RS + rof[st + 1]);
         }
 #pragma unroll
-        for (int qb = 0; qb < T::QB; ++qb) {
-          sacc[qb] = mfma32(qa[qb], kf[st], sacc[qb]);
-          pacc[qb] = mfma32(da[qb], vf[st], pacc[qb]);
-        }
+        for (int qb = 0; qb < T::QB; ++qb) acc1[qb] = mfma32(a[qb], kv[st], acc1[qb]);
         if (st + 1 < T::KS) {
 #pragma unroll
-          for (int qb = 0; qb < T::QB; ++qb) {
-            qa[qb] = qn[qb];
-            da[qb] = dn[qb];
-          }
+          for (int qb = 0; qb < T::QB; ++qb) a[qb] = an[qb];
         }
       }
     }
 
-    // ---- P = exp2(S*c - LSE2) and dS = P * (dP - D), rounded to bf16
-    bf16x8 pb[T::PS], db[T::PS];
+    // ---- A: P = exp2(S*c - LSE2) (causal: keys after the query -> 0), to
+    // its partner through LDS and rounded to bf16 for dV
+    bf16x8 op[T::PS];  // P (A) or dS (B), bf16, MFMA B operand of the second product
+    if (role_a) {
+      // only the first two steps of a causal key block straddle the diagonal
+      const bool need = CAUSAL && (i - i0 < 2);
 #pragma unroll
-    for (int qb = 0; qb < T::QB; ++qb) {
-      // causal: keys after the query are masked; only blocks that straddle the diagonal need it
-      const bool need = CAUSAL && (qs + qb * 32 < kw0 + 31);
+      for (int qb = 0; qb < T::QB; ++qb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sb + T::OFF_LSE + (qb * 32 + 8 * g + 4 * half) * 4);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sb + T::OFF_DD + (qb * 32 + 8 * g + 4 * half) * 4);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(sb + T::OFF_LSE + (qb * 32 + 8 * g + 4 * half) * 4);
+          f32x4 p4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * g + e;
-          float p = exp2_fast(fmaf(sacc[qb][j], c, -l4[e]));
-          if (need && key > qs + qb * 32 + 8 * g + 4 * half + e) p = 0.f;
-          const float ds = p * (pacc[qb][j] - d4[e]);
-          pb[qb * 2 + (j >> 3)][j & 7] = (__bf16)p;
-          db[qb * 2 + (j >> 3)][j & 7] = (__bf16)ds;
+          for (int e = 0; e < 4; ++e) {
+            float p = exp2_fast(fmaf(acc1[qb][4 * g + e], c, -l4[e]));
+            if (need && key > qs + qb * 32 + 8 * g + 4 * half + e) p = 0.f;
+            p4[e] = p;
+            const int j = 4 * g + e;
+            op[qb * 2 + (j >> 3)][j & 7] = (__bf16)p;
+          }
+          *reinterpret_cast<f32x4*>(xp + (qb * 4 + g) * 64 * 16) = p4;
         }
-      }
+    }
+    __syncthreads();  // P of this step is in LDS
+    // ---- B: dS = P * (dP - D), rounded to bf16
+    if (!role_a) {
+#pragma unroll
+      for (int qb = 0; qb < T::QB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(sb + T::OFF_DD + (qb * 32 + 8 * g + 4 * half) * 4);
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(xp + (qb * 4 + g) * 64 * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * g + e;
+            op[qb * 2 + (j >> 3)][j & 7] = (__bf16)(p4[e] * (acc1[qb][j] - d4[e]));
+          }
+        }
     }
 
-    // ---- dV^T += dO^T P,  dK^T += Q^T dS  (k = query, in the accumulator's order);
-    // the transposed operands of the next (ps, b) are read one MFMA pair ahead
+    // ---- second product: dV^T += dO^T P (A) or dK^T += Q^T dS (B), k = query
+    // in the accumulator's order; transposed operands read one MFMA ahead
     {
-      bf16x8 doa = tr_pair(sb + T::OFF_DO, tof[0][0], tof[0][1]);
-      bf16x8 qta = tr_pair(sb, tof[0][0], tof[0][1]);
+      bf16x8 a = tr_pair(sb, tof[0][0], tof[0][1]);
 #pragma unroll
       for (int ps = 0; ps < T::PS; ++ps)
 #pragma unroll
         for (int b = 0; b < T::DB; ++b) {
           const int nb = (b + 1 < T::DB) ? b + 1 : 0;
           const int nps = (b + 1 < T::DB) ? ps : ps + 1;
-          bf16x8 don, qtn;
-          if (nps < T::PS) {
-            don = tr_pair(sb + T::OFF_DO + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
-            qtn = tr_pair(sb + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
-          }
-          dvt[b] = mfma32(doa, pb[ps], dvt[b]);
-          dkt[b] = mfma32(qta, db[ps], dkt[b]);
-          if (nps < T::PS) {
-            doa = don;
-            qta = qtn;
-          }
+          bf16x8 an;
+          if (nps < T::PS) an = tr_pair(sb + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
+          acc2[b] = mfma32(a, op[ps], acc2[b]);
+          if (nps < T::PS) a = an;
         }
     }
 
     // the loads of step i+1 have landed; every wave is done with this stage
+    // and with the P hand-over buffer
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
-  // ---- epilogue: dK = scale * (dK^T)^T, dV = (dV^T)^T; lane holds key `key`,
-  // keys past N are dropped by the buffer bounds
-  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(dK + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(dV + head, head_bytes);
+  // ---- epilogue: dV = (dV^T)^T (A), dK = scale * (dK^T)^T (B); lane holds
+  // key `key`, keys past N are dropped by the buffer bounds
+  const float f = role_a ? 1.f : scale;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((role_a ? dV : dK) + head, head_bytes);
 #pragma unroll
   for (int b = 0; b < T::DB; ++b)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int col = b * 32 + 8 * g + 4 * half;
-      u32x2 wk, wv;
-      wk[0] = pack_bf16x2(dkt[b][4 * g + 0] * scale, dkt[b][4 * g + 1] * scale);
-      wk[1] = pack_bf16x2(dkt[b][4 * g + 2] * scale, dkt[b][4 * g + 3] * scale);
-      wv[0] = pack_bf16x2(dvt[b][4 * g + 0], dvt[b][4 * g + 1]);
-      wv[1] = pack_bf16x2(dvt[b][4 * g + 2], dvt[b][4 * g + 3]);
-      __builtin_amdgcn_raw_buffer_store_b64(wk, rdk, key * T::RS + col * 2, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b64(wv, rdv, key * T::RS + col * 2, 0, 0);
+      u32x2 w;
+      w[0] = pack_bf16x2(acc2[b][4 * g + 0] * f, acc2[b][4 * g + 1] * f);
+      w[1] = pack_bf16x2(acc2[b][4 * g + 2] * f, acc2[b][4 * g + 3] * f);
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, key * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
 }
 
