@@ -30,6 +30,10 @@
 
 namespace fa {
 
+// Largest lead (log2 units) of a tile's row max over the running reference
+// before the reference moves; bounds P by 2^8 = 256.
+constexpr float kLazyRescale = 8.f;
+
 template <int D>
 struct FwdTile {
   static constexpr int NW = 4;                    // waves per workgroup
@@ -180,7 +184,10 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, wave_swap32(mx));
-    const float m_new = fmaxf(m, mx * c);
+    // The reference m moves only when the tile's max exceeds it by more than
+    // kLazyRescale (log2 units), so P <= 2^kLazyRescale and the O and l
+    // rescale is skipped on most tiles; softmax is invariant to the reference.
+    const float m_new = (mx * c > m + kLazyRescale) ? mx * c : m;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet in this row
     const float alpha = exp2_fast(m - m_use);
     m = m_new;

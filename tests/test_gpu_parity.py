@@ -156,6 +156,20 @@ def test_gpt2_shape(gpu_lib, name):
     check_lse(name, _np(lse), rl)
 
 
+@pytest.mark.parametrize("N", [300, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_bf16_many_heads(gpu_lib, N, d, causal):
+    """Many heads of a ragged length: large grids, both head dims, both masks,
+    compared in full."""
+    q, k, v = make_inputs(1, 256, N, d, "bf16", seed=600 + N + d)
+    scale = d ** -0.5
+    o, lse = _fwd(gpu_lib, q, k, v, causal, scale)
+    ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), scale, causal)
+    check_o(f"ragged_bf16_many_heads N={N} d={d} causal={causal}", _np(o), ro)
+    check_lse(f"ragged_bf16_many_heads N={N} d={d} causal={causal}", _np(lse), rl)
+
+
 def test_forward_deterministic(gpu_lib):
     q, k, v = _gpu(*make_inputs(2, 4, 1000, 128, "bf16", seed=7))
     o1, l1 = gpu_lib.fwd(q, k, v, causal=True)
