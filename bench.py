@@ -14,6 +14,9 @@ Prints ONE JSON line.  `value` is the algorithmic TFLOP/s of the step
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -32,6 +35,22 @@ from aware_exact_attention_amd.inputs import WORKLOADS, make_inputs, to_f64  # n
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak at B1 H8 N16K d128; bwd TFLOP/s"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "aware_exact_attention_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_traffic_B1H8N16384d128.txt")
+COPY_BYTES = 1 << 30          # size of the calibration copy (read and written once each)
+# kernels of one step, as named in rocprofv3 output
+FWD_KERNELS = ("fwd_bf16_kernel",)
+BWD_KERNELS = ("bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; traffic counters are only valid for the kernels they were taken on."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -42,9 +61,66 @@ def parse():
     p.add_argument("--workload", default="bwd_16k", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=1, help="heads of the workload the oracle is timed on")
-    p.add_argument("--traffic-json", default=None,
-                   help="measured HBM bytes per launch {'fwd': B, 'bwd_main': B} from rocprofv3 counter runs")
+    p.add_argument("--traffic-json", default=TRAFFIC_FILE,
+                   help="HBM bytes per launch measured with rocprofv3 counters (written by --traffic-from)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain device copy of COPY_BYTES (for the FETCH_SIZE / WRITE_SIZE calibration)")
+    p.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                   help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output of the bench and of --copy-calibration "
+                        "into the traffic summary, then exit")
     return p.parse_args()
+
+
+def _counter_means(d: str, counter: str):
+    """Mean per-dispatch value of `counter` for every kernel in a rocprofv3 counter_collection CSV."""
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def traffic_from(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path):
+    """HBM bytes per launch = FETCH_SIZE + WRITE_SIZE (KiB per dispatch), each scaled by
+    the factor that makes the same counter read COPY_BYTES for a plain copy of COPY_BYTES."""
+    def per_kernel(d, counter):
+        m = _counter_means(d, counter)
+        return {n: sum(v for k, v in m.items() if n in k) * 1024 for n in FWD_KERNELS + BWD_KERNELS}
+
+    def copy_bytes_raw(d, counter):
+        m = _counter_means(d, counter)
+        big = [v for k, v in m.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+        return max(big) * 1024 if big else None
+
+    cf, cw = copy_bytes_raw(copy_fetch_dir, "FETCH_SIZE"), copy_bytes_raw(copy_write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / cf if cf else None
+    w_scale = COPY_BYTES / cw if cw else None
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    res = {"source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES,
+           "copy_fetch_bytes_raw": cf, "copy_write_bytes_raw": cw, "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernels": {}}
+    for group, names in (("fwd", FWD_KERNELS), ("bwd", BWD_KERNELS)):
+        tot = 0.0
+        for n in names:
+            fb, wb = fetch[n] * (f_scale or 1.0), write[n] * (w_scale or 1.0)
+            res["kernels"][n] = {"fetch_bytes": round(fb), "write_bytes": round(wb)}
+            tot += fb + wb
+        res[group] = round(tot)
+    with open(out_path, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(res))
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES bytes, five times."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "calls": 5}))
 
 
 def cpu_baseline(w, q, k, v, do, heads: int):
@@ -78,6 +154,9 @@ def cpu_baseline(w, q, k, v, do, heads: int):
 
 def main():
     a = parse()
+    if a.traffic_from:
+        traffic_from(*a.traffic_from, a.traffic_json)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": a.gpus}))
@@ -85,6 +164,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
     fa.load()
     w = WORKLOADS[a.workload]
     q, k, v, do = make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_std, backward=True)
@@ -128,21 +210,24 @@ def main():
     b_tf = w.bwd_flop / (b_ms * 1e-3) / 1e12
     value = (w.fwd_flop + w.bwd_flop) / (ms_step * 1e-3) / 1e12
 
+    # measured HBM bytes per launch, valid only for the kernel sources they were taken on
     traffic = {}
-    if a.traffic_json and os.path.exists(a.traffic_json):
-        traffic = json.load(open(a.traffic_json))
+    if a.workload == "bwd_16k" and a.traffic_json and os.path.exists(a.traffic_json):
+        t = json.load(open(a.traffic_json))
+        if t.get("source_hash") == kernel_source_hash():
+            traffic = t
 
     def roof(flop, ms, key):
         ach = flop / (ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic.get(key)}
 
-    # the backward (2.5x the forward's FLOPs) is the dominant cost of the step
-    dominant = "bwd" if b_ms >= f_ms else "fwd"
-    r_bwd = roof(w.bwd_flop, b_ms, "bwd_main")
-    r_bwd["kernel"] = "fa_bwd: bwd_main_kernel (+ bwd_pre_kernel, bwd_dq_convert_kernel in the same event pair)"
+    # The backward call (2.5x the forward's algorithmic FLOPs) dominates the step.
+    r_bwd = roof(w.bwd_flop, b_ms, "bwd")
+    r_bwd["kernel"] = ("fa_bwd: bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel (one HIP event pair around the "
+                       "call); FLOP = 10*B*H*N^2*d algorithmic (the dQ pass's recompute of S and dP not counted)")
     r_fwd = roof(w.fwd_flop, f_ms, "fwd")
-    r_fwd["kernel"] = "fa_fwd: fwd_bf16_kernel"
+    r_fwd["kernel"] = "fa_fwd: fwd_bf16_kernel; FLOP = 4*B*H*N^2*d"
     bytes_fwd = w.B * w.H * w.N * (8 * w.d + 4)
     bytes_bwd = w.B * w.H * w.N * (16 * w.d + 12)
 
@@ -167,7 +252,7 @@ def main():
                 "pages_a100_context": "pages: 28.5 ms (38.6 TFLOP/s derived) on an A100 at this shape, forward only"},
         "bwd": {"ms": round(b_ms, 4), "tflops": round(b_tf, 2), "frac_peak": round(b_tf / PEAK_BF16_TFLOPS, 4),
                 "algorithmic_bytes": bytes_bwd},
-        "roofline": r_bwd if dominant == "bwd" else r_fwd,
+        "roofline": r_bwd,
         "roofline_fwd": r_fwd,
     }
     if not a.no_cpu_baseline:
