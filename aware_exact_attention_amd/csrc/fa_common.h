@@ -35,6 +35,11 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 
 __device__ __forceinline__ float wave_swap32(float x) { return __shfl_xor(x, 32); }
 
+// Max and sum over lanes l and l^32 (the two halves of a query row in the
+// MFMA accumulator layout).
+__device__ __forceinline__ float halves_max(float x) { return fmaxf(x, wave_swap32(x)); }
+__device__ __forceinline__ float halves_sum(float x) { return x + wave_swap32(x); }
+
 // XOR swizzle of 16-byte units within an LDS row, chosen so that 16
 // consecutive rows read at the same logical unit hit 16 distinct 16-byte bank
 // groups (and 8 consecutive rows hit 8 distinct groups of a 128-byte window).

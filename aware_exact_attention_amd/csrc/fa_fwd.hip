@@ -141,7 +141,8 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   f32x16 o[T::DB];
 #pragma unroll
   for (int b = 0; b < T::DB; ++b) o[b] = f32x16{};
-  float m = -INFINITY;  // running max of scale*log2(e)*score
+  float m = -INFINITY;  // reference (running max) of scale*log2(e)*score
+  float mu = 0.f;       // m, or 0 while m is -inf: the value subtracted before exp2
   float l = 0.f;        // running sum over this lane's half of the keys
 
   auto compute = [&](int j, const char* base) {
@@ -177,35 +178,41 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
         }
     }
-    // ---- online softmax (scale > 0, so max(score)*c == max(score*c))
+    // ---- online softmax (scale > 0, so max(score)*c == max(score*c)).
+    // The reference m of a row moves only when a tile's row max exceeds it by
+    // more than kLazyRescale (log2 units), so P <= 2^kLazyRescale and the O
+    // and l rescale is skipped on most tiles; softmax is invariant to the
+    // reference.  Each lane tests its own half of the row; only when some
+    // lane of the wave needs a new reference are the halves combined and
+    // the reference, O and l updated.
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, wave_swap32(mx));
-    // The reference m moves only when the tile's max exceeds it by more than
-    // kLazyRescale (log2 units), so P <= 2^kLazyRescale and the O and l
-    // rescale is skipped on most tiles; softmax is invariant to the reference.
-    const float m_new = (mx * c > m + kLazyRescale) ? mx * c : m;
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet in this row
-    const float alpha = exp2_fast(m - m_use);
-    m = m_new;
-    float rs = 0.f;
+    if (__builtin_amdgcn_ballot_w64(mx * c > m + kLazyRescale)) {
+      const float mxr = halves_max(mx) * c;
+      const float m_new = (mxr > m + kLazyRescale) ? mxr : m;
+      const float mu_new = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet in this row
+      const float alpha = exp2_fast(mu - mu_new);  // O and l are still 0 while m is -inf
+      m = m_new;
+      mu = mu_new;
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < T::DB; ++b) o[b] *= alpha;
+    }
+    // P, rounded to bf16 for the PV product; l sums the fp32 values
     bf16x8 pb[T::PS];
+    float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s[kb][r], c, -m_use));
+        const float p = exp2_fast(fmaf(s[kb][r], c, -mu));
         rs += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
-    l = l * alpha + rs;
-    if (alpha != 1.f) {
-#pragma unroll
-      for (int b = 0; b < T::DB; ++b) o[b] *= alpha;
-    }
+    l += rs;
     // ---- O^T += V_j^T P^T: DB independent chains; V^T operands come from two
     // transposing reads of the row-major V tile, one (b, ps) ahead
     auto vread = [&](int b, int ps) {
@@ -248,7 +255,7 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (j < nt) step(j, 0);
 
   if (!wave_active) return;
-  const float lt = l + wave_swap32(l);
+  const float lt = halves_sum(l);
   const float inv = 1.f / lt;
   // rows past N are dropped by the buffer bounds
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head, head_bytes);
