@@ -10,7 +10,8 @@
 // Software 2026(1) p.218 survey.  The per-row statistic written for the
 // backward pass is LSE = m + ln(l).
 //
-// gfx950 mapping of the bf16 kernel (one workgroup = 4 waves = 128 query rows):
+// gfx950 mapping of the bf16 kernel (one workgroup = 4 or 8 waves = 128 or
+// 256 query rows, two waves per SIMD either way):
 //  * each wave owns 32 whole query rows, so the row statistics m and l never
 //    leave the wave (no inter-wave exchange);
 //  * the wave computes S^T = K_j Q_i^T with v_mfma_f32_32x32x16_bf16: the
@@ -34,9 +35,12 @@ namespace fa {
 // before the reference moves; bounds P by 2^8 = 256.
 constexpr float kLazyRescale = 8.f;
 
-template <int D>
+// Compute units of a gfx950 device (MI355X / MI350X).
+constexpr long long kNumCUs = 256;
+
+template <int D, int NW_>
 struct FwdTile {
-  static constexpr int NW = 4;                    // waves per workgroup
+  static constexpr int NW = NW_;                  // waves per workgroup (4 or 8; two waves per SIMD either way)
   static constexpr int NT = 64 * NW;              // threads per workgroup
   static constexpr int BR = 32 * NW;              // query rows per workgroup
   static constexpr int BC = 64;                   // keys per KV tile
@@ -51,12 +55,12 @@ struct FwdTile {
   static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                 int N, int Tr, float c) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, NW>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
   const int tid = threadIdx.x;
@@ -369,17 +373,31 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                                    int B, int H, int N, float scale, hipStream_t st) {
-  using T = FwdTile<D>;
+template <int D, bool CAUSAL, int NW>
+static hipError_t launch_fwd_bf16_nw(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int B, int H, int N, float scale, hipStream_t st) {
+  using T = FwdTile<D, NW>;
   const int Tr = (N + T::BR - 1) / T::BR;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(T::NT), 0, st,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)G), dim3(T::NT), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
                      scale * kLog2e);
   return hipGetLastError();
+}
+
+// Eight waves (256 rows, one workgroup per CU) stream each K/V tile once for
+// twice the rows of four waves (128 rows, two workgroups per CU), halving the
+// tile loads and LDS writes per row; used at d = 128 when that grid still
+// covers every CU.  Causal launches keep 128-row tiles (their per-tile work is
+// uneven and finer tiles balance it better), and so does d = 64, whose tiles
+// carry half the MFMA work per barrier (measured slower with 8 waves).
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int B, int H, int N, float scale, hipStream_t st) {
+  const long long G8 = (long long)B * H * ((N + FwdTile<D, 8>::BR - 1) / FwdTile<D, 8>::BR);
+  if (D == 128 && !CAUSAL && G8 >= kNumCUs) return launch_fwd_bf16_nw<D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, st);
+  return launch_fwd_bf16_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, N, scale, st);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
