@@ -344,9 +344,9 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
 // ---------------------------------------------------------------------------
 // 3. dQ: query-block-major sweep over the keys
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NW_>
 struct DqTile {
-  static constexpr int NW = 4;
+  static constexpr int NW = NW_;                  // 4 or 8 waves; two waves per SIMD either way
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;              // queries per workgroup
   static constexpr int BC = 64;                   // keys per tile
@@ -361,12 +361,12 @@ struct DqTile {
   static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
               const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
               __bf16* __restrict__ dQ, int N, int Tr, float c /* scale*log2(e) */, float scale) {
-  using T = DqTile<D>;
+  using T = DqTile<D, NW>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
   const int tid = threadIdx.x;
@@ -565,7 +565,12 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
 
   const int Tk = (N + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV;
   const long long Gk = (long long)B * H * Tk;
-  const int Tr = (N + DqTile<D>::BR - 1) / DqTile<D>::BR;
+  // dQ pass: eight waves (256 rows) per workgroup for non-causal d = 128 grids
+  // that cover every CU (each K/V tile streamed once for twice the rows), as
+  // in the forward; four waves otherwise.
+  const long long Gq8 = (long long)B * H * ((N + DqTile<D, 8>::BR - 1) / DqTile<D, 8>::BR);
+  const bool dq8 = D == 128 && !CAUSAL && Gq8 >= kNumCUs;
+  const int Tr = dq8 ? (N + DqTile<D, 8>::BR - 1) / DqTile<D, 8>::BR : (N + DqTile<D, 4>::BR - 1) / DqTile<D, 4>::BR;
   const long long Gq = (long long)B * H * Tr;
   if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
@@ -573,9 +578,14 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                      (const float*)lse2, (const float*)Dv, (__bf16*)dk, (__bf16*)dv, N, Tk, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)Gq), dim3(DqTile<D>::NT), 0, st,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                     (const float*)lse2, (const float*)Dv, (__bf16*)dq, N, Tr, c, scale);
+  if (dq8)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 8>), dim3((unsigned)Gq), dim3(DqTile<D, 8>::NT), 0, st,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
+                       (const float*)lse2, (const float*)Dv, (__bf16*)dq, N, Tr, c, scale);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 4>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT), 0, st,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
+                       (const float*)lse2, (const float*)Dv, (__bf16*)dq, N, Tr, c, scale);
   return hipGetLastError();
 }
 

@@ -18,6 +18,10 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Compute units of a gfx950 device (MI355X / MI350X); used to decide whether
+// a grid of large workgroups still covers the whole GPU.
+constexpr long long kNumCUs = 256;
+
 // v_mfma_f32_32x32x16_bf16.  Lane l supplies row (l % 32) of A and column
 // (l % 32) of B, each with eight k-values; lanes l and l+32 together cover
 // the 16 k-values, with the same k assignment for A and B, so any fixed

@@ -35,9 +35,6 @@ namespace fa {
 // before the reference moves; bounds P by 2^8 = 256.
 constexpr float kLazyRescale = 8.f;
 
-// Compute units of a gfx950 device (MI355X / MI350X).
-constexpr long long kNumCUs = 256;
-
 template <int D, int NW_>
 struct FwdTile {
   static constexpr int NW = NW_;                  // waves per workgroup (4 or 8; two waves per SIMD either way)

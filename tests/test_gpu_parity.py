@@ -233,6 +233,20 @@ def test_bwd_small(gpu_lib, N, d, causal):
     check_grad(tag, "dV", dv, rv)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ragged_many_heads(gpu_lib, causal):
+    """256 heads of 300 rows: a grid large enough for the 256-row dQ
+    workgroups (non-causal, d = 128), with a ragged tail in every head."""
+    q, k, v, do = make_inputs(1, 256, 300, 128, "bf16", seed=450, backward=True)
+    scale = 128 ** -0.5
+    _, _, dq, dk, dv = _bwd_case(gpu_lib, q, k, v, do, causal, scale)
+    rq, rk, rv = oracle.ref_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal)
+    tag = f"bwd many heads N=300 d=128 causal={causal}"
+    check_grad(tag, "dQ", dq, rq)
+    check_grad(tag, "dK", dk, rk)
+    check_grad(tag, "dV", dv, rv)
+
+
 @pytest.mark.parametrize("name,heads", [("fwd_bwd_causal", [(0, 0), (1, 7), (3, 15)]), ("bwd_16k", [(0, 5)])])
 def test_full_size_backward_sampled_heads(gpu_lib, name, heads):
     w = WORKLOADS[name]
