@@ -453,34 +453,40 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
       p[kb] = f32x16{};
     }
     {
-      bf16x8 ka[T::KB], va[T::KB];
+      // K and V operands are read KPF k steps ahead, an order pinned by
+      // scheduling barriers (left alone, the scheduler pulls each read next to
+      // its MFMA and the LDS latency shows)
+      constexpr int KPF = 2;
+      bf16x8 ka[KPF][T::KB], va[KPF][T::KB];
+      auto rd = [&](int st, int kb, int v) {
+        return *reinterpret_cast<const bf16x8*>(base + v * T::TILE + kb * 32 * T::RS + rof[st]);
+      };
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-        ka[kb] = *reinterpret_cast<const bf16x8*>(base + kb * 32 * T::RS + rof[0]);
-        va[kb] = *reinterpret_cast<const bf16x8*>(base + T::TILE + kb * 32 * T::RS + rof[0]);
-      }
-#pragma unroll
-      for (int st = 0; st < T::KS; ++st) {
-        bf16x8 kn[T::KB], vn[T::KB];
-        if (st + 1 < T::KS) {
-#pragma unroll
-          for (int kb = 0; kb < T::KB; ++kb) {
-            kn[kb] = *reinterpret_cast<const bf16x8*>(base + kb * 32 * T::RS + rof[st + 1]);
-            vn[kb] = *reinterpret_cast<const bf16x8*>(base + T::TILE + kb * 32 * T::RS + rof[st + 1]);
-          }
-        }
+      for (int st = 0; st < KPF; ++st)
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) {
-          s[kb] = mfma32(ka[kb], qf[st], s[kb]);
-          p[kb] = mfma32(va[kb], df[st], p[kb]);
+          ka[st][kb] = rd(st, kb, 0);
+          va[st][kb] = rd(st, kb, 1);
         }
-        if (st + 1 < T::KS) {
+#pragma unroll
+      for (int st = 0; st < T::KS; ++st) {
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) {
+          s[kb] = mfma32(ka[st % KPF][kb], qf[st], s[kb]);
+          p[kb] = mfma32(va[st % KPF][kb], df[st], p[kb]);
+        }
+        if (st + KPF < T::KS)
 #pragma unroll
           for (int kb = 0; kb < T::KB; ++kb) {
-            ka[kb] = kn[kb];
-            va[kb] = vn[kb];
+            ka[st % KPF][kb] = rd(st + KPF, kb, 0);
+            va[st % KPF][kb] = rd(st + KPF, kb, 1);
           }
-        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::KB * KPF, 0);
+#pragma unroll
+      for (int st = 0; st < T::KS; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::KB, 0);
+        if (st + KPF < T::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::KB, 0);
       }
     }
     // ---- dS^T = P^T * (dP^T - D) with P^T = exp2(S^T*c - LSE2), rounded to bf16.

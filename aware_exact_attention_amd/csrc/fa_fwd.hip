@@ -35,6 +35,7 @@ namespace fa {
 // before the reference moves; bounds P by 2^8 = 256.
 constexpr float kLazyRescale = 8.f;
 
+
 template <int D, int NW_>
 struct FwdTile {
   static constexpr int NW = NW_;                  // waves per workgroup (4 or 8; two waves per SIMD either way)
@@ -147,23 +148,31 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   float l = 0.f;        // running sum over this lane's half of the keys
 
   auto compute = [&](int j, const char* base) {
-    // ---- S^T = K_j Q^T: two independent 32-key chains, K operands read one step ahead
+    // ---- S^T = K_j Q^T: two independent 32-key chains; K operands are read
+    // KPF k steps ahead, an order pinned by scheduling barriers (left alone,
+    // the scheduler pulls each read next to its MFMA and the LDS latency shows)
     f32x16 s0 = f32x16{}, s1 = f32x16{};
-    bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(base + kof[0]);
-    bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(base + kof[0] + 32 * T::RS);
+    constexpr int KPF = 2;
+    bf16x8 kr[KPF][2];
+#pragma unroll
+    for (int st = 0; st < KPF; ++st) {
+      kr[st][0] = *reinterpret_cast<const bf16x8*>(base + kof[st]);
+      kr[st][1] = *reinterpret_cast<const bf16x8*>(base + kof[st] + 32 * T::RS);
+    }
 #pragma unroll
     for (int st = 0; st < T::KS; ++st) {
-      bf16x8 kn0, kn1;
-      if (st + 1 < T::KS) {
-        kn0 = *reinterpret_cast<const bf16x8*>(base + kof[st + 1]);
-        kn1 = *reinterpret_cast<const bf16x8*>(base + kof[st + 1] + 32 * T::RS);
+      s0 = mfma32(kr[st % KPF][0], qf[st], s0);
+      s1 = mfma32(kr[st % KPF][1], qf[st], s1);
+      if (st + KPF < T::KS) {
+        kr[st % KPF][0] = *reinterpret_cast<const bf16x8*>(base + kof[st + KPF]);
+        kr[st % KPF][1] = *reinterpret_cast<const bf16x8*>(base + kof[st + KPF] + 32 * T::RS);
       }
-      s0 = mfma32(ka0, qf[st], s0);
-      s1 = mfma32(ka1, qf[st], s1);
-      if (st + 1 < T::KS) {
-        ka0 = kn0;
-        ka1 = kn1;
-      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KPF, 0);
+#pragma unroll
+    for (int st = 0; st < T::KS; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (st + KPF < T::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     f32x16 s[2] = {s0, s1};
     // ---- masks: keys past N and, if causal, keys after the query
@@ -215,7 +224,7 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       }
     l += rs;
     // ---- O^T += V_j^T P^T: DB independent chains; V^T operands come from two
-    // transposing reads of the row-major V tile, one (b, ps) ahead
+    // transposing reads of the row-major V tile, VPF operands ahead
     auto vread = [&](int b, int ps) {
       const char* vb = base + ps * 16 * T::RS;
       const bf16x4 lo = __builtin_bit_cast(
@@ -224,18 +233,17 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(vb + vof[b][1])));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    bf16x8 va = vread(0, 0);
+    constexpr int VPF = 3;  // V operands in flight, in (ps, b) order
+    constexpr int NV = T::PS * T::DB;
+    bf16x8 vr[VPF];
 #pragma unroll
-    for (int ps = 0; ps < T::PS; ++ps)
+    for (int u = 0; u < VPF; ++u) vr[u] = vread(u % T::DB, u / T::DB);
 #pragma unroll
-      for (int b = 0; b < T::DB; ++b) {
-        const int nb = (b + 1 < T::DB) ? b + 1 : 0;
-        const int nps = (b + 1 < T::DB) ? ps : ps + 1;
-        bf16x8 vn;
-        if (nps < T::PS) vn = vread(nb, nps);
-        o[b] = mfma32(va, pb[ps], o[b]);
-        if (nps < T::PS) va = vn;
-      }
+    for (int u = 0; u < NV; ++u) {
+      const int ps = u / T::DB, b = u % T::DB;
+      o[b] = mfma32(vr[u % VPF], pb[ps], o[b]);
+      if (u + VPF < NV) vr[u % VPF] = vread((u + VPF) % T::DB, (u + VPF) / T::DB);
+    }
   };
 
   auto step = [&](int j, int stage) {
