@@ -5,3 +5,4 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 Python binding never do, and this package imports nothing from them.
 """
 from .ref import ref_bwd, ref_bwd_delta, ref_fwd, ref_fwd_rows, ref_probs  # noqa: F401
+from .split import ref_fwd_keyrange, ref_lse_merge  # noqa: F401
