@@ -14,6 +14,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int d, float scale, int causal, hipStream_t st);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                           int N, int d, float scale, int causal, hipStream_t st);
+hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                              int N, int d, float scale, int causal, int S, void* ws, hipStream_t st);
+hipError_t launch_lse_merge(const float* op, const float* lp, int S, void* o, float* lse, int B, int H, int N,
+                            int d, hipStream_t st);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                       int causal, void* ws, hipStream_t st);
@@ -77,6 +81,40 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (st != fa::kOk) return st;
   return fa::launch_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, workspace, stream) ==
                  hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
+  return fa::split_workspace_bytes(fa::Shape{B, H, N, d}, num_splits);
+}
+
+int fa_fwd_splitkv_parts(int B, int H, int N, int d, int num_splits) {
+  return fa::split_count(fa::Shape{B, H, N, d}, num_splits);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_fwd_splitkv(q, k, v, o, lse, s, scale, causal, num_splits, workspace, workspace_bytes);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  const int S = fa::split_count(s, num_splits);
+  return fa::launch_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, S, workspace, stream) == hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_lse_merge(const float* o_parts, const float* lse_parts, int num_parts, void* o, float* lse, int B, int H,
+                 int N, int d, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_lse_merge(o_parts, lse_parts, num_parts, o, lse, s);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_lse_merge(o_parts, lse_parts, num_parts, o, lse, B, H, N, d, stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
 }

@@ -53,11 +53,23 @@ struct FwdTile {
   static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
 
-template <int D, bool CAUSAL, int NW>
+// Key-split mode: the keys of every row are cut into ranges of TPS whole
+// tiles; part p of a row covers tiles [p*TPS, (p+1)*TPS).  Each part writes
+// its normalised output in fp32 to OP[p][B][H][N][d] and its log-sum-exp to
+// LP[p][B][H][N]; a row that sees no key in its range gets O = 0 and
+// LSE = -inf.  The parts are merged by lse_merge_kernel (Eq. (2)).
+struct SplitArgs {
+  int S, TPS;
+  float* OP;
+  float* LP;
+  long long part_elems, part_rows;  // B*H*N*d and B*H*N
+};
+
+template <int D, bool CAUSAL, int NW, bool SPLIT>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
 fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-                int N, int Tr, float c) {
+                int N, int Tr, float c, SplitArgs sp) {
   using T = FwdTile<D, NW>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
@@ -67,8 +79,11 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / Tr;
-  int it = tile - bh * Tr;
+  const int per_head = SPLIT ? Tr * sp.S : Tr;  // the parts of a query block are adjacent
+  const int bh = tile / per_head;
+  const int rem = tile - bh * per_head;
+  const int part = SPLIT ? rem % sp.S : 0;
+  int it = SPLIT ? rem / sp.S : rem;
   if (CAUSAL) it = Tr - 1 - it;  // longest rows first
   const int q0 = it * T::BR;
   const size_t head = size_t(bh) * N * D;
@@ -95,6 +110,13 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const bool wave_active = wq0 < N;
   int nt_w = nt;
   if (CAUSAL && wave_active) nt_w = min(nt, (min(wq0 + 32, N) - 1) / T::BC + 1);
+  // this workgroup's tiles: [j0, nt); each wave computes [j0, nt_w)
+  int j0 = 0;
+  if (SPLIT) {
+    j0 = part * sp.TPS;
+    nt = min(nt, j0 + sp.TPS);
+    nt_w = min(nt_w, nt);
+  }
 
   // Direct-to-LDS tile loads: load i of this wave fills LDS bytes
   // [(wave*LPW + i) KiB, +1 KiB) of the tile; lane l brings the 16 bytes that
@@ -253,18 +275,37 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __syncthreads();
   };
 
-  issue_loads(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  int j = 0;
-  for (; j + 1 < nt; j += 2) {
-    step(j, 0);
-    step(j + 1, 1);
+  if (j0 < nt) {  // uniform over the workgroup; an empty key part skips the sweep
+    issue_loads(j0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    int j = j0;
+    for (; j + 1 < nt; j += 2) {
+      step(j, 0);
+      step(j + 1, 1);
+    }
+    if (j < nt) step(j, 0);
   }
-  if (j < nt) step(j, 0);
 
   if (!wave_active) return;
   const float lt = halves_sum(l);
+  if (SPLIT) {
+    // normalised fp32 part; rows that saw no key: O = 0, LSE = -inf
+    const float pinv = lt > 0.f ? 1.f / lt : 0.f;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(sp.OP + size_t(part) * sp.part_elems + head, N * D * 4);
+#pragma unroll
+    for (int b = 0; b < T::DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(unsigned, o[b][4 * g + e] * pinv);
+        __builtin_amdgcn_raw_buffer_store_b128(w, rp, qrow * D * 4 + (b * 32 + 8 * g + 4 * half) * 4, 0, 0);
+      }
+    if (half == 0 && qrow < N)
+      sp.LP[size_t(part) * sp.part_rows + size_t(bh) * N + qrow] = lt > 0.f ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
+    return;
+  }
   const float inv = 1.f / lt;
   // rows past N are dropped by the buffer bounds
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head, head_bytes);
@@ -385,9 +426,9 @@ static hipError_t launch_fwd_bf16_nw(const void* q, const void* k, const void* v
   const int Tr = (N + T::BR - 1) / T::BR;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)G), dim3(T::NT), 0, st,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, false>), dim3((unsigned)G), dim3(T::NT), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
-                     scale * kLog2e);
+                     scale * kLog2e, SplitArgs{1, 0, nullptr, nullptr, 0, 0});
   return hipGetLastError();
 }
 
@@ -411,6 +452,115 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                               : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, B, H, N, scale, st);
   return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, B, H, N, scale, st)
                 : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, B, H, N, scale, st);
+}
+
+// ---------------------------------------------------------------------------
+// Eq. (2) merge of S parts: for each row, with M = max_s LSE_s and
+// w_s = e^(LSE_s - M): O = sum_s w_s O_s / sum_s w_s (rounded once to bf16)
+// and LSE = M + ln sum_s w_s.  Parts with LSE_s = -inf weigh 0; a row whose
+// parts are all -inf gets O = 0, LSE = -inf.  HBM-bound: D/8 lanes per row,
+// each lane reads 8 consecutive floats of every part (two 16-byte loads) and
+// writes 8 bf16 (one 16-byte store).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256)
+lse_merge_kernel(const float* __restrict__ OP, const float* __restrict__ LP, int S,
+                 __bf16* __restrict__ O, float* __restrict__ LSE, long long rows) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / LPR;
+  const int sub = int(t % LPR);
+  if (row >= rows) return;
+  // parts in groups of G: all loads of a group are issued before any use
+  constexpr int G = 8;
+  float M = -INFINITY;
+  for (int p0 = 0; p0 < S; p0 += G) {
+    float lp[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) lp[g] = LP[min(p0 + g, S - 1) * rows + row];  // past S: a repeat of part S-1
+#pragma unroll
+    for (int g = 0; g < G; ++g) M = fmaxf(M, lp[g]);
+  }
+  f32x4 a0 = {}, a1 = {};
+  float L = 0.f;
+  if (M > -INFINITY) {
+    for (int p0 = 0; p0 < S; p0 += G) {
+      float lp[G];
+      f32x4 x0[G], x1[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        // loads clamped to part S-1 (always in bounds); parts past S weigh 0 below
+        const int pc = min(p0 + g, S - 1);
+        const float l_in = LP[pc * rows + row];
+        lp[g] = p0 + g < S ? l_in : -INFINITY;
+        const f32x4* src = reinterpret_cast<const f32x4*>(OP + (pc * rows + row) * D + sub * 8);
+        x0[g] = src[0];
+        x1[g] = src[1];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        // a part that saw no key weighs 0 (its O is ignored)
+        const float w = lp[g] > -INFINITY ? exp2_fast((lp[g] - M) * kLog2e) : 0.f;
+        a0 += w * x0[g];
+        a1 += w * x1[g];
+        L += w;
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  u32x4 w;
+  w[0] = pack_bf16x2(a0[0] * inv, a0[1] * inv);
+  w[1] = pack_bf16x2(a0[2] * inv, a0[3] * inv);
+  w[2] = pack_bf16x2(a1[0] * inv, a1[1] * inv);
+  w[3] = pack_bf16x2(a1[2] * inv, a1[3] * inv);
+  *reinterpret_cast<u32x4*>(O + row * D + sub * 8) = w;
+  if (sub == 0) LSE[row] = L > 0.f ? M + log2_fast(L) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_lse_merge(const float* op, const float* lp, int S, void* o, float* lse, int B, int H, int N,
+                            int d, hipStream_t st) {
+  const long long rows = (long long)B * H * N;
+  const long long threads = rows * (d / 8);
+  const long long blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (d == 128)
+    hipLaunchKernelGGL((lse_merge_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
+                       lse, rows);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
+                       lse, rows);
+  return hipGetLastError();
+}
+
+// Key-split forward: S parts per query block (four-wave workgroups), then the
+// merge.  S == 1 is the plain forward.
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                     int H, int N, float scale, int S, void* ws, hipStream_t st) {
+  if (S <= 1) return launch_fwd_bf16_t<D, CAUSAL>(q, k, v, o, lse, B, H, N, scale, st);
+  using T = FwdTile<D, 4>;
+  const SplitLayout w = split_workspace_layout(Shape{B, H, N, D}, S);
+  const int Tr = (N + T::BR - 1) / T::BR;
+  const int Tc = (N + T::BC - 1) / T::BC;
+  const long long G = (long long)B * H * Tr * S;
+  if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  char* base = reinterpret_cast<char*>(ws);
+  SplitArgs sp{S, (Tc + S - 1) / S, reinterpret_cast<float*>(base + w.o_parts),
+               reinterpret_cast<float*>(base + w.lse_parts), (long long)B * H * N * D, (long long)B * H * N};
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, true>), dim3((unsigned)G), dim3(T::NT), 0, st,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
+                     scale * kLog2e, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_lse_merge(sp.OP, sp.LP, S, o, lse, B, H, N, D, st);
+}
+
+hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                              int N, int d, float scale, int causal, int S, void* ws, hipStream_t st) {
+  if (d == 128) return causal ? launch_fwd_split_t<128, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
+                              : launch_fwd_split_t<128, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
+  return causal ? launch_fwd_split_t<64, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
+                : launch_fwd_split_t<64, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
 }
 
 template <int D, bool CAUSAL>

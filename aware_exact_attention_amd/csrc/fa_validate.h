@@ -115,6 +115,102 @@ inline int validate_bwd(const void* q, const void* k, const void* v, const void*
   return kOk;
 }
 
+// ---------------------------------------------------------------------------
+// Key-split forward and the merge of parts
+// ---------------------------------------------------------------------------
+// The split forward runs four-wave workgroups of 128 query rows over 64-key
+// tiles; a part is a range of whole tiles.
+constexpr int kSplitKeyTile = 64;
+constexpr int kSplitRowBlock = 128;
+constexpr int kMaxSplits = 64;
+// Automatic choice: enough parts for two four-wave workgroups on each of the
+// 256 CUs, at least two tiles per part, at most 16 parts.
+constexpr long long kSplitTargetWorkgroups = 512;
+constexpr int kMaxAutoSplits = 16;
+constexpr int kMaxMergeParts = 4096;
+
+// Number of key parts fa_fwd_splitkv uses for `requested` (<= 0: automatic),
+// or 0 if the shape is invalid.  Parts that would hold no tile are dropped.
+inline int split_count(const Shape& s, int requested) {
+  if (tensor_elems(s) < 0 || (s.d != 64 && s.d != 128)) return 0;
+  const int tc = (s.N + kSplitKeyTile - 1) / kSplitKeyTile;
+  long long S;
+  if (requested > 0) {
+    S = requested;
+  } else {
+    const long long g = (long long)s.B * s.H * ((s.N + kSplitRowBlock - 1) / kSplitRowBlock);
+    S = g >= kSplitTargetWorkgroups ? 1 : (kSplitTargetWorkgroups + g - 1) / g;
+    const long long two_tiles = tc / 2 > 0 ? tc / 2 : 1;
+    if (S > two_tiles) S = two_tiles;
+    if (S > kMaxAutoSplits) S = kMaxAutoSplits;
+  }
+  if (S > tc) S = tc;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S < 1) S = 1;
+  const long long tps = (tc + S - 1) / S;
+  return int((tc + tps - 1) / tps);
+}
+
+// Workspace of the split forward with S > 1 parts, each part rounded up to
+// 256 bytes: fp32 partial outputs [S][B][H][N][d], then fp32 partial
+// log-sum-exps [S][B][H][N].  S <= 1 needs none.
+struct SplitLayout {
+  size_t o_parts, lse_parts, total;
+};
+
+inline SplitLayout split_workspace_layout(const Shape& s, int S) {
+  if (S <= 1 || tensor_elems(s) < 0) return SplitLayout{0, 0, 0};
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = size_t(s.B) * s.H * s.N;
+  SplitLayout w;
+  w.o_parts = 0;
+  w.lse_parts = up(size_t(S) * rows * s.d * 4);
+  w.total = w.lse_parts + up(size_t(S) * rows * 4);
+  return w;
+}
+
+inline size_t split_workspace_bytes(const Shape& s, int requested) {
+  return split_workspace_layout(s, split_count(s, requested)).total;
+}
+
+inline int validate_fwd_splitkv(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                                const Shape& s, float scale, int causal, int requested, const void* ws,
+                                size_t ws_bytes) {
+  int st = validate_fwd(q, k, v, o, lse, s, scale, causal, 2);
+  if (st != kOk) return st;
+  const int S = split_count(s, requested);
+  if (S > 1) {
+    const size_t need = split_workspace_layout(s, S).total;
+    if (!ws || ws_bytes < need) return kErrWorkspace;
+    if (!aligned16(ws)) return kErrAlign;
+    const size_t tb = size_t(tensor_elems(s)) * 2;
+    const size_t lb = size_t(s.B) * s.H * s.N * sizeof(float);
+    const void* all[5] = {q, k, v, o, lse};
+    const size_t sz[5] = {tb, tb, tb, tb, lb};
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(ws, need, all[i], sz[i])) return kErrArg;
+  }
+  return kOk;
+}
+
+// Merge: o_parts float [S][B][H][N][d], lse_parts float [S][B][H][N] in;
+// o bf16 [B][H][N][d], lse float [B][H][N] out.
+inline int validate_lse_merge(const void* o_parts, const void* lse_parts, int S, const void* o, const void* lse,
+                              const Shape& s) {
+  if (!o_parts || !lse_parts || !o || !lse) return kErrNull;
+  if (tensor_elems(s) < 0) return kErrShape;
+  if (s.d != 64 && s.d != 128) return kErrHeadDim;
+  if (S < 1 || S > kMaxMergeParts) return kErrArg;
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse)) return kErrAlign;
+  const size_t rows = size_t(s.B) * s.H * s.N;
+  const size_t ob = rows * s.d * 2, lb = rows * 4;
+  const size_t opb = size_t(S) * rows * s.d * 4, lpb = size_t(S) * rows * 4;
+  if (overlaps(o, ob, o_parts, opb) || overlaps(o, ob, lse_parts, lpb) || overlaps(lse, lb, o_parts, opb) ||
+      overlaps(lse, lb, lse_parts, lpb) || overlaps(o, ob, lse, lb))
+    return kErrArg;
+  return kOk;
+}
+
 inline const char* status_string(int st) {
   switch (st) {
     case kOk: return "FA_OK: success";
@@ -123,10 +219,10 @@ inline const char* status_string(int st) {
     case kErrHeadDim: return "FA_ERR_HEAD_DIM: head dimension d must be 64 or 128";
     case kErrScale: return "FA_ERR_SCALE: scale must be finite and > 0";
     case kErrAlign: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
-    case kErrWorkspace: return "FA_ERR_WORKSPACE: workspace missing or smaller than fa_bwd_workspace_bytes()";
+    case kErrWorkspace: return "FA_ERR_WORKSPACE: workspace missing or smaller than the *_workspace_bytes() size";
     case kErrDevice: return "FA_ERR_DEVICE: the current device is not a gfx950 GPU";
     case kErrHip: return "FA_ERR_HIP: a HIP launch or runtime call failed";
-    case kErrArg: return "FA_ERR_ARG: causal must be 0 or 1 and outputs must not alias inputs";
+    case kErrArg: return "FA_ERR_ARG: causal must be 0 or 1, a part count in range, and outputs must not alias inputs";
     default: return "unknown fa_status";
   }
 }

@@ -27,6 +27,11 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "fa_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
                         _c_int, _vp, _c_size_t, _vp]),
+    "fa_fwd_splitkv_parts": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "fa_fwd_splitkv_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "fa_fwd_splitkv": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int,
+                                _vp, _c_size_t, _vp]),
+    "fa_lse_merge": (_c_int, [_vp, _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -147,3 +152,75 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, w
     if st != 0:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def splitkv_parts(B: int, H: int, N: int, d: int, num_splits: int = 0) -> int:
+    return int(load().fa_fwd_splitkv_parts(B, H, N, d, int(num_splits)))
+
+
+def splitkv_workspace_bytes(B: int, H: int, N: int, d: int, num_splits: int = 0) -> int:
+    return int(load().fa_fwd_splitkv_workspace_bytes(B, H, N, d, int(num_splits)))
+
+
+def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0,
+                workspace=None, out=None, lse=None):
+    """bf16 forward with the keys split into parallel parts merged by Eq. (2); returns ``(o, lse)``.
+
+    ``num_splits <= 0`` lets the library choose.  ``workspace`` (uint8 GPU
+    tensor of at least ``splitkv_workspace_bytes`` bytes) is allocated if not
+    given.
+    """
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,N,d]")
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, (B, H, N, d))
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, N))
+    need = splitkv_workspace_bytes(B, H, N, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8)
+    st = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                            float(scale), int(bool(causal)), int(num_splits),
+                            workspace.data_ptr() if workspace is not None else None,
+                            workspace.numel() if workspace is not None else 0, _stream())
+    if st != 0:
+        raise FAError(st, "fa_fwd_splitkv")
+    return out, lse
+
+
+def lse_merge(o_parts, lse_parts, out=None, lse=None):
+    """Eq. (2) merge of ``o_parts`` float32 ``[S,B,H,N,d]`` and ``lse_parts`` float32 ``[S,B,H,N]``.
+
+    Returns ``(o, lse)``: bf16 ``[B,H,N,d]`` and float32 ``[B,H,N]``.
+    """
+    lib = load()
+    if o_parts.dim() != 5:
+        raise ValueError("o_parts must be [S,B,H,N,d]")
+    S, B, H, N, d = o_parts.shape
+    _check(o_parts, "o_parts", torch.float32, (S, B, H, N, d))
+    _check(lse_parts, "lse_parts", torch.float32, (S, B, H, N))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=o_parts.device)
+    else:
+        _check(out, "out", torch.bfloat16, (B, H, N, d))
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, N))
+    st = lib.fa_lse_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                          _stream())
+    if st != 0:
+        raise FAError(st, "fa_lse_merge")
+    return out, lse

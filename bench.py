@@ -60,6 +60,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="bwd_16k", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-next-rows", action="store_true", help="skip the split-KV / merge measurements")
     p.add_argument("--cpu-heads", type=int, default=1, help="heads of the workload the oracle is timed on")
     p.add_argument("--traffic-json", default=TRAFFIC_FILE,
                    help="HBM bytes per launch measured with rocprofv3 counters (written by --traffic-from)")
@@ -150,6 +151,69 @@ def cpu_baseline(w, q, k, v, do, heads: int):
                   f"(N={w.N}, d={w.d}); fwd {t1 - t0:.2f} s, bwd {t2 - t1:.2f} s; TFLOP/s of that sample",
         "host_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def _graph_ms(fn, calls: int, warmup: int = 3) -> float:
+    """GPU time per call of `fn`: `calls` back-to-back calls captured in one HIP
+    graph, replayed 5 times between HIP events (median), so that host-side call
+    overhead does not show in the times of kernels of a few microseconds.  The
+    library's calls allocate nothing and only launch kernels, so they capture."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    rounds = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rounds.append(e0.elapsed_time(e1) / calls)
+    return sorted(rounds)[len(rounds) // 2]
+
+
+def next_rows():
+    """Key-split forward (fa_fwd_splitkv) against fa_fwd on grids too small to fill
+    the GPU, and the Eq. (2) merge kernel (fa_lse_merge) against the HBM roof."""
+    res = {}
+    for name, (B, H, N, d, causal) in {"B1H8N2048d128": (1, 8, 2048, 128, False),
+                                       "B1H4N4096d128_causal": (1, 4, 4096, 128, True),
+                                       "B1H2N8192d64": (1, 2, 8192, 64, False)}.items():
+        q, k, v = (t.cuda() for t in make_inputs(B, H, N, d, "bf16", 9, 1.0))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        parts = fa.splitkv_parts(B, H, N, d, 0)
+        ws = torch.empty(max(fa.splitkv_workspace_bytes(B, H, N, d, 0), 16), dtype=torch.uint8, device="cuda")
+        flop = 4 * B * H * N * N * d / (2 if causal else 1)
+        t_f = _graph_ms(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse), 20)
+        t_s = _graph_ms(lambda: fa.fwd_splitkv(q, k, v, causal=causal, workspace=ws, out=o, lse=lse), 20)
+        assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+        res[name] = {"parts": parts, "fa_fwd_ms": round(t_f, 5), "fa_fwd_splitkv_ms": round(t_s, 5),
+                     "speedup": round(t_f / t_s, 3), "splitkv_tflops": round(flop / (t_s * 1e-3) / 1e12, 1),
+                     "splitkv_frac_peak": round(flop / (t_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    # merge kernel alone: S = 4 parts of B1 H8 N2048 d128
+    S, B, H, N, d = 4, 1, 8, 2048, 128
+    g = torch.Generator().manual_seed(9)
+    op = torch.randn((S, B, H, N, d), generator=g).cuda()
+    lp = torch.randn((S, B, H, N), generator=g).cuda()
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    t_m = _graph_ms(lambda: fa.lse_merge(op, lp, out=o, lse=lse), 50)
+    rows = B * H * N
+    mbytes = S * rows * d * 4 + S * rows * 4 + rows * d * 2 + rows * 4
+    gbs = mbytes / (t_m * 1e-3) / 1e9
+    res["lse_merge_S4_B1H8N2048d128"] = {"ms": round(t_m, 5), "algorithmic_bytes": mbytes,
+                                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                                      "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    return res
 
 
 def main():
@@ -255,6 +319,8 @@ def main():
         "roofline": r_bwd,
         "roofline_fwd": r_fwd,
     }
+    if not a.no_next_rows:
+        out["next_rows"] = next_rows()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, a.cpu_heads)
     print(json.dumps(out), flush=True)

@@ -56,10 +56,10 @@ typedef enum {
   FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 */
   FA_ERR_SCALE = -4,     /* scale not finite or not > 0 */
   FA_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
-  FA_ERR_WORKSPACE = -6, /* backward workspace missing or smaller than fa_bwd_workspace_bytes() */
+  FA_ERR_WORKSPACE = -6, /* workspace missing or smaller than the matching *_workspace_bytes() */
   FA_ERR_DEVICE = -7,    /* current device is not gfx950, or its properties cannot be read */
   FA_ERR_HIP = -8,       /* a HIP launch or runtime call failed */
-  FA_ERR_ARG = -9        /* causal not 0/1, or outputs alias inputs */
+  FA_ERR_ARG = -9        /* causal not 0/1, a part count out of range, or outputs alias inputs */
 } fa_status;
 
 /*
@@ -112,6 +112,66 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const void* dO, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_fwd_splitkv_parts - number of key parts fa_fwd_splitkv uses for these
+ * sizes and this num_splits (<= 0: automatic), or 0 if the sizes are
+ * invalid.  The keys of every row are cut into ranges of whole 64-key tiles;
+ * a request is capped at the number of tiles and at 64, and parts that would
+ * hold no tile are dropped.  The automatic choice aims at 512 workgroups of
+ * 128 query rows (two per CU), with at least two tiles per part and at most
+ * 16 parts; grids that already have 512 workgroups get 1 part.
+ */
+int fa_fwd_splitkv_parts(int B, int H, int N, int d, int num_splits);
+
+/*
+ * fa_fwd_splitkv_workspace_bytes - bytes of workspace fa_fwd_splitkv needs:
+ * fp32 partial outputs [S][B][H][N][d] and fp32 partial log-sum-exps
+ * [S][B][H][N] for S = fa_fwd_splitkv_parts(...) parts, each rounded up to
+ * 256 bytes.  Returns 0 when S is 1 (no workspace needed) or the sizes are
+ * invalid.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
+
+/*
+ * fa_fwd_splitkv - bf16 forward attention with exactly the inputs, outputs
+ * and conventions of fa_fwd, computed with the keys of every row split into
+ * S = fa_fwd_splitkv_parts(B,H,N,d,num_splits) ranges that separate
+ * workgroups process in parallel; each range yields a normalised partial
+ * output (fp32) and its log-sum-exp, and the parts are then merged by Eq. (2)
+ * of the Journal of Software 2026(1) p.218 survey (as fa_lse_merge does).
+ * For grids too small to fill the GPU (few heads, short sequences) this
+ * keeps every CU busy.  S == 1 runs fa_fwd's kernel and needs no workspace.
+ * workspace: device buffer of at least fa_fwd_splitkv_workspace_bytes(...)
+ * bytes (may be NULL when that is 0), owned by the caller, 16-byte aligned,
+ * not overlapping any tensor argument; contents on entry do not matter.
+ * Results agree with fa_fwd to rounding (the fp32 partials add one more
+ * rounding step), not bit for bit.
+ * Errors: as fa_fwd, plus FA_ERR_WORKSPACE (missing or too small).
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal, int num_splits,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_lse_merge - merge S partial attention results over disjoint key sets by
+ * Eq. (2) of the Journal of Software 2026(1) p.218 survey: for every row,
+ * with M = max_s lse_parts[s] and w_s = e^(lse_parts[s] - M),
+ *   o   = sum_s w_s o_parts[s] / sum_s w_s   (fp32, rounded once to bf16),
+ *   lse = M + ln sum_s w_s.
+ * o_parts: float [S][B][H][N][d], each part normalised by its own sum;
+ * lse_parts: float [S][B][H][N], natural-log log-sum-exp of each part (-inf
+ * for a row that saw no key in that part: such a part is ignored).  o:
+ * __bf16 [B][H][N][d] and lse: float [B][H][N] outputs; a row whose parts
+ * are all -inf gets o = 0 and lse = -inf.  S = num_parts in [1, 4096].
+ * This is the single-GPU half of attention over keys sharded across devices:
+ * each shard's fa_fwd output, converted to fp32, is one part.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_ALIGN,
+ * FA_ERR_ARG (num_parts out of range or outputs overlapping inputs),
+ * FA_ERR_DEVICE, FA_ERR_HIP.
+ */
+int fa_lse_merge(const float* o_parts, const float* lse_parts, int num_parts, void* o, float* lse,
+                 int B, int H, int N, int d, hipStream_t stream);
 
 /* fa_status_string - static, human-readable text for a status code. */
 const char* fa_status_string(int status);

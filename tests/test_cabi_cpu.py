@@ -38,7 +38,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_bytes", "fa_bwd",
-                                           "fa_status_string"])
+                                           "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_bytes",
+                                           "fa_fwd_splitkv", "fa_lse_merge", "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -138,6 +139,64 @@ def test_bwd_validation(lib):
     assert call(ws=dq) == ST["ARG"]          # workspace aliases an output
 
 
+def test_splitkv_parts_and_workspace(lib):
+    parts = lib.fa_fwd_splitkv_parts
+    # automatic: 8 heads of 16 query blocks = 128 workgroups -> 4 parts reach 512
+    assert parts(1, 8, 2048, 128, 0) == 4
+    assert parts(1, 8, 16384, 128, 0) == 1      # 1024 workgroups already
+    assert parts(1, 1, 256, 64, 0) == 2         # 4 tiles: at least two per part
+    assert parts(1, 1, 64, 64, 0) == 1          # one tile
+    assert parts(1, 1, 4096, 64, 0) == 16       # 32 workgroups, 64 tiles: 16 parts of 4
+    assert parts(1, 1, 2816, 64, 0) == 15       # wants 24, capped at 16: 44 tiles in parts of 3 fill 15
+    assert parts(1, 1, 8192, 64, 0) == 8        # 64 workgroups
+    # requests: capped at the tile count, parts without tiles dropped
+    assert parts(1, 8, 2048, 128, 5) == 5       # 32 tiles: 7,7,7,7,4
+    assert parts(1, 1, 640, 64, 100) == 10
+    assert parts(1, 1, 576, 64, 4) == 3         # 9 tiles, 3 per part
+    assert parts(1, 1, 1 << 20, 64, 1000) == 64
+    assert parts(0, 1, 64, 64, 2) == 0 and parts(1, 1, 64, 96, 2) == 0
+    ws = lib.fa_fwd_splitkv_workspace_bytes
+    rows = 8 * 2048
+    assert ws(1, 8, 2048, 128, 0) == 4 * rows * 128 * 4 + 4 * rows * 4
+    assert ws(1, 8, 16384, 128, 0) == 0
+    assert ws(1, 1, 100, 64, 2) == (2 * 100 * 64 * 4 + 255) // 256 * 256 + (2 * 100 * 4 + 255) // 256 * 256
+    assert ws(1, 1, 100, 80, 2) == 0
+
+
+def test_splitkv_validation(lib):
+    B, H, N, d = 1, 1, 256, 64
+    bufs = [_Buf(B * H * N * d * 2) for _ in range(4)] + [_Buf(B * H * N * 4)]
+    q, k, v, o, l = [b.ptr for b in bufs]
+    need = lib.fa_fwd_splitkv_workspace_bytes(B, H, N, d, 2)
+    assert need > 0
+    wsb = _Buf(need)
+    f = lib.fa_fwd_splitkv
+    assert f(None, k, v, o, l, B, H, N, d, 0.125, 0, 2, wsb.ptr, need, None) == ST["NULL"]
+    assert f(q, k, v, o, l, B, H, N, 96, 0.125, 0, 2, wsb.ptr, need, None) == ST["HEAD_DIM"]
+    assert f(q, k, v, o, l, B, H, N, d, 0.0, 0, 2, wsb.ptr, need, None) == ST["SCALE"]
+    assert f(q, k, v, o, l, B, H, N, d, 0.125, 3, 2, wsb.ptr, need, None) == ST["ARG"]
+    assert f(q, k, v, o, l, B, H, N, d, 0.125, 0, 2, None, 0, None) == ST["WORKSPACE"]
+    assert f(q, k, v, o, l, B, H, N, d, 0.125, 0, 2, wsb.ptr, need - 1, None) == ST["WORKSPACE"]
+    assert f(q, k, v, o, l, B, H, N, d, 0.125, 0, 2, wsb.ptr + 8, need, None) == ST["ALIGN"]
+    assert f(q, k, v, o, l, B, H, N, d, 0.125, 0, 2, o, need, None) == ST["ARG"]  # workspace over an output
+
+
+def test_lse_merge_validation(lib):
+    S, B, H, N, d = 3, 1, 2, 8, 64
+    op, lp = _Buf(S * B * H * N * d * 4), _Buf(S * B * H * N * 4)
+    o, l = _Buf(B * H * N * d * 2), _Buf(B * H * N * 4)
+    f = lib.fa_lse_merge
+    assert f(None, lp.ptr, S, o.ptr, l.ptr, B, H, N, d, None) == ST["NULL"]
+    assert f(op.ptr, lp.ptr, S, o.ptr, None, B, H, N, d, None) == ST["NULL"]
+    assert f(op.ptr, lp.ptr, S, o.ptr, l.ptr, B, 0, N, d, None) == ST["SHAPE"]
+    assert f(op.ptr, lp.ptr, S, o.ptr, l.ptr, B, H, N, 32, None) == ST["HEAD_DIM"]
+    assert f(op.ptr, lp.ptr, 0, o.ptr, l.ptr, B, H, N, d, None) == ST["ARG"]
+    assert f(op.ptr, lp.ptr, 5000, o.ptr, l.ptr, B, H, N, d, None) == ST["ARG"]
+    assert f(op.ptr + 4, lp.ptr, S, o.ptr, l.ptr, B, H, N, d, None) == ST["ALIGN"]
+    assert f(op.ptr, lp.ptr, S, op.ptr + 64, l.ptr, B, H, N, d, None) == ST["ARG"]  # output inside the parts
+    assert f(op.ptr, lp.ptr, S, o.ptr, o.ptr, B, H, N, d, None) == ST["ARG"]        # lse over o
+
+
 def test_validate_header_with_gxx(tmp_path):
     """Host unit test of fa_validate.h compiled by g++ (no HIP, no GPU)."""
     src = tmp_path / "t.cpp"
@@ -174,6 +233,24 @@ int main() {
   EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[6], mem[8], s, 0.125f, 1,
                       ws, sizeof ws) == kErrArg);
   EXPECT(overlaps(mem[0], 16, mem[0] + 15, 1) && !overlaps(mem[0], 16, mem[0] + 16, 1));
+  EXPECT(split_count(Shape{1, 8, 2048, 128}, 0) == 4);
+  EXPECT(split_count(Shape{1, 8, 2048, 128}, 1) == 1);
+  EXPECT(split_count(Shape{1, 1, 576, 64}, 4) == 3);
+  EXPECT(split_count(Shape{1, 1, 64, 65}, 2) == 0);
+  EXPECT(split_workspace_layout(s, 1).total == 0);
+  EXPECT(split_workspace_layout(s, 2).lse_parts == 2 * 32 * 64 * 4);
+  EXPECT(split_workspace_layout(s, 2).total == 2 * 32 * 64 * 4 + 256);
+  EXPECT(validate_fwd_splitkv(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 0, 1, nullptr, 0) == kOk);
+  alignas(16) static char big[6][65536];
+  const Shape s2{1, 1, 256, 64};
+  const size_t need2 = split_workspace_layout(s2, 2).total;
+  EXPECT(need2 == 2 * 256 * 64 * 4 + 2 * 256 * 4);
+  EXPECT(validate_fwd_splitkv(big[0], big[1], big[2], big[3], big[4], s2, 0.125f, 0, 2, nullptr, 0) == kErrWorkspace);
+  EXPECT(validate_fwd_splitkv(big[0], big[1], big[2], big[3], big[4], s2, 0.125f, 0, 2, big[5], 65536) == kErrWorkspace);
+  EXPECT(need2 > 65536);  // so the 64 KiB buffer above is too small
+  EXPECT(validate_lse_merge(mem[0], mem[1], 2, mem[2], mem[3], Shape{1, 1, 8, 64}) == kOk);
+  EXPECT(validate_lse_merge(mem[0], mem[1], 0, mem[2], mem[3], Shape{1, 1, 8, 64}) == kErrArg);
+  EXPECT(validate_lse_merge(mem[0], mem[1], 2, mem[0] + 64, mem[3], Shape{1, 1, 8, 64}) == kErrArg);
   return fails ? 1 : 0;
 }
 ''')
