@@ -1,0 +1,93 @@
+"""fp64 oracle for attention under sliding-window and block-sparse masks.
+
+TEST INFRASTRUCTURE ONLY (same rule as ``oracle/ref.py``).
+
+The pages name two ways of skipping whole blocks of the score matrix: a
+sliding window around each query (the FlashAttention-2 principle and
+deployment page, section on SDPA usage, passes ``window_size=(512, 512)``) and
+block-sparse FlashAttention (FlashAttention optimisation page, section 7;
+Journal of Software survey, the sparse-attention sentence after Eq. (2)).
+Neither page defines the mask precisely; the readings written out here are:
+
+* sliding window ``(left, right)``: key j is visible to query i iff
+  ``i - left <= j <= i + right``; a negative bound means no limit on that
+  side, so ``(-1, -1)`` is dense attention and ``(-1, 0)`` is the causal mask.
+  Every query sees at least itself.
+* block-sparse: the N x N score matrix is cut into 64 x 64 blocks (query block
+  ``i // 64``, key block ``j // 64``); ``block_mask[h][qb][kb] != 0`` keeps the
+  block, 0 drops it.  With ``causal`` the usual ``j <= i`` applies on top.
+
+Within the visible set the computation is the plain definition of
+``oracle/ref.py``.  A row with no visible key (possible only with a block
+mask) has an empty softmax; its output is taken as ``O = 0`` and its
+log-sum-exp as ``-inf`` (the sum over an empty set is 0).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .ref import _as_f64
+
+MASK_BLOCK = 64
+
+
+def window_visible(N: int, left: int, right: int) -> np.ndarray:
+    """``[N, N]`` bool: key j visible to query i iff i-left <= j <= i+right (negative = unlimited)."""
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    vis = np.ones((N, N), dtype=bool)
+    if left >= 0:
+        vis &= j >= i - left
+    if right >= 0:
+        vis &= j <= i + right
+    return vis
+
+
+def blocksparse_visible(N: int, block_mask: np.ndarray, causal: bool) -> np.ndarray:
+    """``[N, N]`` bool from a ``[nb, nb]`` block mask of 64 x 64 blocks (plus j <= i if causal)."""
+    bm = np.asarray(block_mask) != 0
+    qb = np.arange(N) // MASK_BLOCK
+    vis = bm[qb[:, None], qb[None, :]]
+    if causal:
+        vis &= np.arange(N)[None, :] <= np.arange(N)[:, None]
+    return vis
+
+
+def ref_fwd_visible(q, k, v, scale: float, visible):
+    """Attention with an explicit visibility matrix ``[N,N]`` (all heads) or ``[H,N,N]``.
+
+    Returns ``(O [B,H,N,d], LSE [B,H,N])`` in float64; rows with no visible
+    key get ``O = 0`` and ``LSE = -inf``.
+    """
+    q, k, v = _as_f64(q, k, v)
+    B, H, N, _ = q.shape
+    visible = np.asarray(visible, dtype=bool)
+    o = np.zeros((B, H, N, v.shape[-1]))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            vis = visible if visible.ndim == 2 else visible[h]
+            s = np.where(vis, scale * (q[b, h] @ k[b, h].T), -np.inf)
+            m = s.max(axis=1)
+            seen = m > -np.inf
+            if not seen.any():
+                continue
+            f = np.exp(s[seen] - m[seen, None])
+            l = f.sum(axis=1)
+            o[b, h, seen] = (f @ v[b, h]) / l[:, None]
+            lse[b, h, seen] = m[seen] + np.log(l)
+    return o, lse
+
+
+def ref_fwd_window(q, k, v, scale: float, left: int, right: int):
+    """Sliding-window attention; see the module notes for the reading of the window."""
+    return ref_fwd_visible(q, k, v, scale, window_visible(np.shape(q)[2], left, right))
+
+
+def ref_fwd_blocksparse(q, k, v, scale: float, causal: bool, block_mask):
+    """Block-sparse attention; ``block_mask`` is ``[nb,nb]`` (every head) or ``[H,nb,nb]``."""
+    N = np.shape(q)[2]
+    bm = np.asarray(block_mask)
+    if bm.ndim == 2:
+        return ref_fwd_visible(q, k, v, scale, blocksparse_visible(N, bm, causal))
+    return ref_fwd_visible(q, k, v, scale, np.stack([blocksparse_visible(N, m, causal) for m in bm]))
