@@ -91,3 +91,44 @@ def ref_fwd_blocksparse(q, k, v, scale: float, causal: bool, block_mask):
     if bm.ndim == 2:
         return ref_fwd_visible(q, k, v, scale, blocksparse_visible(N, bm, causal))
     return ref_fwd_visible(q, k, v, scale, np.stack([blocksparse_visible(N, m, causal) for m in bm]))
+
+
+def _rows_fwd(q, k, v, scale: float, vis):
+    """One head: attention of the query rows whose visibility rows are ``vis [R, N]``."""
+    s = np.where(vis, scale * (q @ k.T), -np.inf)
+    m = s.max(axis=1)
+    o = np.zeros((s.shape[0], v.shape[-1]))
+    lse = np.full(s.shape[0], -np.inf)
+    seen = m > -np.inf
+    if seen.any():
+        f = np.exp(s[seen] - m[seen, None])
+        l = f.sum(axis=1)
+        o[seen] = (f @ v) / l[:, None]
+        lse[seen] = m[seen] + np.log(l)
+    return o, lse
+
+
+def ref_fwd_window_rows(q, k, v, scale: float, left: int, right: int, rows):
+    """Sliding-window attention of one head ``[N,d]`` for the query rows ``rows`` only."""
+    q, k, v = _as_f64(q, k, v)
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(k.shape[0])[None, :]
+    i = rows[:, None]
+    vis = np.ones((rows.size, k.shape[0]), dtype=bool)
+    if left >= 0:
+        vis &= j >= i - left
+    if right >= 0:
+        vis &= j <= i + right
+    return _rows_fwd(q[rows], k, v, scale, vis)
+
+
+def ref_fwd_blocksparse_rows(q, k, v, scale: float, causal: bool, block_mask, rows):
+    """Block-sparse attention of one head ``[N,d]`` (``block_mask [nb,nb]``) for ``rows`` only."""
+    q, k, v = _as_f64(q, k, v)
+    rows = np.asarray(rows, dtype=np.int64)
+    bm = np.asarray(block_mask) != 0
+    kb = np.arange(k.shape[0]) // MASK_BLOCK
+    vis = bm[(rows // MASK_BLOCK)[:, None], kb[None, :]]
+    if causal:
+        vis &= np.arange(k.shape[0])[None, :] <= rows[:, None]
+    return _rows_fwd(q[rows], k, v, scale, vis)

@@ -110,8 +110,30 @@ def pin_blocksparse_empty_rows_and_heads(M):
     assert np.all(lse2[0, 1, :64] == -np.inf)
 
 
+def pin_row_variants_match(M):
+    """The row-subset versions (used on workloads too large for full N x N) agree
+    with the full ones, themselves pinned above."""
+    N = 200
+    q, k, v = _rand((1, 1, N, 6), 250, 1.5), _rand((1, 1, N, 6), 251, 1.5), _rand((1, 1, N, 6), 252)
+    rows = np.array([0, 1, 63, 64, 65, 127, 150, 199])
+    for left, right in ((10, 3), (-1, 0), (0, -1)):
+        o, lse = M.ref_fwd_window(q, k, v, 0.4, left, right)
+        orow, lrow = M.ref_fwd_window_rows(q[0, 0], k[0, 0], v[0, 0], 0.4, left, right, rows)
+        np.testing.assert_allclose(orow, o[0, 0, rows], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lrow, lse[0, 0, rows], rtol=0, atol=1e-14)
+    bm = (np.random.default_rng(253).random((4, 4)) < 0.5).astype(np.uint8)
+    bm[1] = 0
+    for causal in (False, True):
+        o, lse = M.ref_fwd_blocksparse(q, k, v, 0.4, causal, bm)
+        orow, lrow = M.ref_fwd_blocksparse_rows(q[0, 0], k[0, 0], v[0, 0], 0.4, causal, bm, rows)
+        np.testing.assert_allclose(orow, o[0, 0, rows], rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(np.isinf(lrow), np.isinf(lse[0, 0, rows]))
+        fin = np.isfinite(lrow)
+        np.testing.assert_allclose(lrow[fin], lse[0, 0, rows][fin], rtol=0, atol=1e-14)
+
+
 PINS = [pin_window_limits, pin_window_brute_force, pin_window_constant_keys, pin_blocksparse_limits,
-        pin_blocksparse_empty_rows_and_heads]
+        pin_blocksparse_empty_rows_and_heads, pin_row_variants_match]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
