@@ -18,6 +18,11 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               int N, int d, float scale, int causal, int S, void* ws, hipStream_t st);
 hipError_t launch_lse_merge(const float* op, const float* lp, int S, void* o, float* lse, int B, int H, int N,
                             int d, hipStream_t st);
+hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                             int d, float scale, int left, int right, hipStream_t st);
+hipError_t launch_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                  int N, int d, float scale, int causal, const unsigned char* bm, int per_head,
+                                  hipStream_t st);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                       int causal, void* ws, hipStream_t st);
@@ -115,6 +120,33 @@ int fa_lse_merge(const float* o_parts, const float* lse_parts, int num_parts, vo
   st = fa::check_device();
   if (st != fa::kOk) return st;
   return fa::launch_lse_merge(o_parts, lse_parts, num_parts, o, lse, B, H, N, d, stream) == hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                  float scale, int window_left, int window_right, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_fwd_window(q, k, v, o, lse, s, scale);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_fwd_window(q, k, v, o, lse, B, H, N, d, scale, window_left, window_right, stream) ==
+                 hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                       int d, float scale, int causal, const unsigned char* block_mask, int mask_per_head,
+                       hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_fwd_blocksparse(q, k, v, o, lse, s, scale, causal, block_mask, mask_per_head);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, mask_per_head,
+                                    stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
 }

@@ -65,13 +65,33 @@ struct SplitArgs {
   long long part_elems, part_rows;  // B*H*N*d and B*H*N
 };
 
-template <int D, bool CAUSAL, int NW, bool SPLIT>
+// Tile-skipping masks (beyond causal).  kMaskWindow: key j is visible to
+// query i iff i - left <= j <= i + right (a negative bound: no limit on that
+// side).  kMaskBlocks: bm[h][i / 64][j / 64] != 0 keeps the 64 x 64 block,
+// with the causal mask on top when CAUSAL; bm_head_stride is 0 when all
+// heads share one mask.
+enum : int { kMaskDense = 0, kMaskWindow = 1, kMaskBlocks = 2 };
+constexpr int kMaskBlock = 64;
+constexpr int kMaxMaskTiles = 1024;  // block-sparse: N <= 65536
+struct MaskArgs {
+  int left, right;
+  const unsigned char* bm;
+  long long bm_head_stride;
+  int nb, H;
+};
+
+template <int D, bool CAUSAL, int NW, bool SPLIT, int MODE>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
 fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-                int N, int Tr, float c, SplitArgs sp) {
+                int N, int Tr, float c, SplitArgs sp, MaskArgs mk) {
   using T = FwdTile<D, NW>;
+  constexpr bool WINDOW = MODE == kMaskWindow, BLOCKS = MODE == kMaskBlocks;
+  static_assert(!(SPLIT && MODE != kMaskDense), "key split only with the dense or causal mask");
+  static_assert(!BLOCKS || (T::BC == kMaskBlock && T::BR == 2 * kMaskBlock), "mask blocks are key tiles and half a row block");
   __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+  __shared__ unsigned short tlist[BLOCKS ? kMaxMaskTiles : 1];
+  __shared__ int tcount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,13 +130,51 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const bool wave_active = wq0 < N;
   int nt_w = nt;
   if (CAUSAL && wave_active) nt_w = min(nt, (min(wq0 + 32, N) - 1) / T::BC + 1);
-  // this workgroup's tiles: [j0, nt); each wave computes [j0, nt_w)
-  int j0 = 0;
+  // this workgroup's tiles: [j0, nt); each wave computes [w0, nt_w)
+  int j0 = 0, w0 = 0;
   if (SPLIT) {
     j0 = part * sp.TPS;
     nt = min(nt, j0 + sp.TPS);
     nt_w = min(nt_w, nt);
   }
+  if (WINDOW) {
+    // tiles that hold a key of the band [i - left, i + right] of some row i
+    const int lo = mk.left >= 0 ? max(0, q0 - mk.left) : 0;
+    const int hi = mk.right >= 0 ? min(N, q0 + T::BR + mk.right) : N;  // exclusive
+    j0 = lo / T::BC;
+    nt = (hi - 1) / T::BC + 1;
+    w0 = mk.left >= 0 ? max(0, wq0 - mk.left) / T::BC : 0;
+    nt_w = mk.right >= 0 ? (min(N, wq0 + 32 + mk.right) - 1) / T::BC + 1 : Tc;
+  }
+  // block-sparse: the workgroup's tiles, in order, in tlist[0 .. tcount); a
+  // wave computes a tile only if its own 64-row block keeps it
+  const unsigned char* bm_row = nullptr;
+  if (BLOCKS) {
+    const int h = bh % mk.H;
+    const unsigned char* bmh = mk.bm + mk.bm_head_stride * h;
+    bm_row = bmh + size_t(min(wq0, N - 1) / kMaskBlock) * mk.nb;
+    if (wave == 0) {
+      const unsigned char* r0 = bmh + size_t(q0 / kMaskBlock) * mk.nb;
+      const bool two = q0 + kMaskBlock < N;  // the workgroup's second 64-row block exists
+      int n = 0;
+      for (int base = 0; base < nt; base += 64) {
+        const int jj = base + lane;
+        const bool keep = jj < nt && (r0[jj] != 0 || (two && r0[mk.nb + jj] != 0));
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(keep);
+        const int below = __builtin_popcountll(bal & ((1ull << lane) - 1));
+        if (keep) tlist[n + below] = (unsigned short)jj;
+        n += __builtin_popcountll(bal);
+      }
+      if (lane == 0) tcount = n;
+    }
+    __syncthreads();
+  }
+  const int cnt = BLOCKS ? tcount : nt - j0;
+  auto tile_at = [&](int idx) { return BLOCKS ? int(tlist[idx]) : j0 + idx; };
+  auto wave_needs = [&](int j) {
+    if (!wave_active || j >= nt_w || j < w0) return false;
+    return !BLOCKS || bm_row[j] != 0;
+  };
 
   // Direct-to-LDS tile loads: load i of this wave fills LDS bytes
   // [(wave*LPW + i) KiB, +1 KiB) of the tile; lane l brings the 16 bytes that
@@ -197,17 +255,23 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       if (st + KPF < T::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     f32x16 s[2] = {s0, s1};
-    // ---- masks: keys past N and, if causal, keys after the query
+    // ---- masks: keys past N and, if causal, keys after the query; for a
+    // window, keys outside [qrow - left, qrow + right].  Only tiles that cross
+    // one of these edges for some row of the wave pay for the element mask.
     const int key0 = j * T::BC;
     bool need = key0 + T::BC > N;
     if (CAUSAL) need = need || (key0 + T::BC - 1 > wq0);
+    if (WINDOW)
+      need = need || (mk.left >= 0 && key0 < wq0 + 31 - mk.left) || (mk.right >= 0 && key0 + T::BC - 1 > wq0 + mk.right);
     if (need) {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + acc_row(r, lane);
-          if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+          bool hide = key >= N || (CAUSAL && key > qrow);
+          if (WINDOW) hide = hide || (mk.left >= 0 && key < qrow - mk.left) || (mk.right >= 0 && key > qrow + mk.right);
+          if (hide) s[kb][r] = -INFINITY;
         }
     }
     // ---- online softmax (scale > 0, so max(score)*c == max(score*c)).
@@ -268,23 +332,25 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   };
 
-  auto step = [&](int j, int stage) {
-    if (j + 1 < nt) issue_loads(j + 1, stage ^ 1);
-    if (wave_active && j < nt_w) compute(j, smem + stage * T::STAGE);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j+1 have landed
+  // step idx: tile tile_at(idx) from stage `stage`, loads of the next tile into the other
+  auto step = [&](int idx, int stage) {
+    if (idx + 1 < cnt) issue_loads(tile_at(idx + 1), stage ^ 1);
+    const int j = tile_at(idx);
+    if (wave_needs(j)) compute(j, smem + stage * T::STAGE);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the next tile have landed
     __syncthreads();
   };
 
-  if (j0 < nt) {  // uniform over the workgroup; an empty key part skips the sweep
-    issue_loads(j0, 0);
+  if (cnt > 0) {  // uniform over the workgroup; an empty key part or mask row skips the sweep
+    issue_loads(tile_at(0), 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    int j = j0;
-    for (; j + 1 < nt; j += 2) {
-      step(j, 0);
-      step(j + 1, 1);
+    int idx = 0;
+    for (; idx + 1 < cnt; idx += 2) {
+      step(idx, 0);
+      step(idx + 1, 1);
     }
-    if (j < nt) step(j, 0);
+    if (idx < cnt) step(idx, 0);
   }
 
   if (!wave_active) return;
@@ -306,7 +372,8 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       sp.LP[size_t(part) * sp.part_rows + size_t(bh) * N + qrow] = lt > 0.f ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
     return;
   }
-  const float inv = 1.f / lt;
+  // a row that saw no key (block-sparse masks only): O = 0, LSE = -inf
+  const float inv = (!BLOCKS || lt > 0.f) ? 1.f / lt : 0.f;
   // rows past N are dropped by the buffer bounds
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head, head_bytes);
 #pragma unroll
@@ -318,7 +385,7 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       w[1] = pack_bf16x2(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
       __builtin_amdgcn_raw_buffer_store_b64(w, ro, qrow * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
-  if (half == 0 && qrow < N) LSE[size_t(bh) * N + qrow] = (m + log2_fast(lt)) * kLn2;
+  if (half == 0 && qrow < N) LSE[size_t(bh) * N + qrow] = (!BLOCKS || lt > 0.f) ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -426,9 +493,9 @@ static hipError_t launch_fwd_bf16_nw(const void* q, const void* k, const void* v
   const int Tr = (N + T::BR - 1) / T::BR;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, false>), dim3((unsigned)G), dim3(T::NT), 0, st,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, false, kMaskDense>), dim3((unsigned)G), dim3(T::NT), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
-                     scale * kLog2e, SplitArgs{1, 0, nullptr, nullptr, 0, 0});
+                     scale * kLog2e, SplitArgs{1, 0, nullptr, nullptr, 0, 0}, MaskArgs{});
   return hipGetLastError();
 }
 
@@ -547,9 +614,9 @@ static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v
   char* base = reinterpret_cast<char*>(ws);
   SplitArgs sp{S, (Tc + S - 1) / S, reinterpret_cast<float*>(base + w.o_parts),
                reinterpret_cast<float*>(base + w.lse_parts), (long long)B * H * N * D, (long long)B * H * N};
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, true>), dim3((unsigned)G), dim3(T::NT), 0, st,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, true, kMaskDense>), dim3((unsigned)G), dim3(T::NT), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
-                     scale * kLog2e, sp);
+                     scale * kLog2e, sp, MaskArgs{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_lse_merge(sp.OP, sp.LP, S, o, lse, B, H, N, D, st);
@@ -561,6 +628,40 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               : launch_fwd_split_t<128, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
   return causal ? launch_fwd_split_t<64, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
                 : launch_fwd_split_t<64, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
+}
+
+// Sliding-window and block-sparse forwards: four-wave workgroups (128 rows,
+// two 64-row mask blocks), the same kernel with a per-tile predicate.
+template <int D, bool CAUSAL, int MODE>
+static hipError_t launch_fwd_masked_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                      int H, int N, float scale, const MaskArgs& mk, hipStream_t st) {
+  using T = FwdTile<D, 4>;
+  const int Tr = (N + T::BR - 1) / T::BR;
+  const long long G = (long long)B * H * Tr;
+  if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, false, MODE>), dim3((unsigned)G), dim3(T::NT), 0, st,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
+                     scale * kLog2e, SplitArgs{1, 0, nullptr, nullptr, 0, 0}, mk);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                             int d, float scale, int left, int right, hipStream_t st) {
+  const MaskArgs mk{left, right, nullptr, 0, 0, H};
+  if (d == 128) return launch_fwd_masked_t<128, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  return launch_fwd_masked_t<64, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
+}
+
+hipError_t launch_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                  int N, int d, float scale, int causal, const unsigned char* bm, int per_head,
+                                  hipStream_t st) {
+  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+  const MaskArgs mk{-1, -1, bm, per_head ? (long long)nb * nb : 0, nb, H};
+  if (d == 128)
+    return causal ? launch_fwd_masked_t<128, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
+                  : launch_fwd_masked_t<128, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  return causal ? launch_fwd_masked_t<64, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
+                : launch_fwd_masked_t<64, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
 }
 
 template <int D, bool CAUSAL>

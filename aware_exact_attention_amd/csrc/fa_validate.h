@@ -211,6 +211,40 @@ inline int validate_lse_merge(const void* o_parts, const void* lse_parts, int S,
   return kOk;
 }
 
+// ---------------------------------------------------------------------------
+// Tile-skipping masks
+// ---------------------------------------------------------------------------
+constexpr int kMaskBlockRows = 64;        // block-sparse masks are over 64 x 64 blocks
+constexpr int kMaxBlockSparseN = 65536;   // the kernel lists at most 1024 key blocks per row block
+
+inline int validate_fwd_window(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                               const Shape& s, float scale) {
+  return validate_fwd(q, k, v, o, lse, s, scale, 0, 2);
+}
+
+// Bytes of the block mask: [H][nb][nb] (per_head) or [nb][nb], nb = ceil(N/64).
+inline size_t block_mask_bytes(const Shape& s, int per_head) {
+  const size_t nb = size_t(s.N + kMaskBlockRows - 1) / kMaskBlockRows;
+  return (per_head ? size_t(s.H) : 1) * nb * nb;
+}
+
+inline int validate_fwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                                    const Shape& s, float scale, int causal, const void* block_mask,
+                                    int per_head) {
+  if (!block_mask || !q || !k || !v || !o || !lse) return kErrNull;
+  int st = check_common(s, scale, causal);
+  if (st != kOk) return st;
+  if (s.N > kMaxBlockSparseN) return kErrShape;
+  if (per_head != 0 && per_head != 1) return kErrArg;
+  st = validate_fwd(q, k, v, o, lse, s, scale, causal, 2);
+  if (st != kOk) return st;
+  const size_t mb = block_mask_bytes(s, per_head);
+  const size_t tb = size_t(tensor_elems(s)) * 2;
+  const size_t lb = size_t(s.B) * s.H * s.N * sizeof(float);
+  if (overlaps(block_mask, mb, o, tb) || overlaps(block_mask, mb, lse, lb)) return kErrArg;
+  return kOk;
+}
+
 inline const char* status_string(int st) {
   switch (st) {
     case kOk: return "FA_OK: success";

@@ -32,6 +32,10 @@ SIGNATURES = {
     "fa_fwd_splitkv": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int,
                                 _vp, _c_size_t, _vp]),
     "fa_lse_merge": (_c_int, [_vp, _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "fa_fwd_window": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int,
+                               _vp]),
+    "fa_fwd_blocksparse": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp,
+                                    _c_int, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -223,4 +227,62 @@ def lse_merge(o_parts, lse_parts, out=None, lse=None):
                           _stream())
     if st != 0:
         raise FAError(st, "fa_lse_merge")
+    return out, lse
+
+
+def _fwd_outputs(q, out, lse):
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, (B, H, N, d))
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, N))
+    return out, lse
+
+
+def fwd_window(q, k, v, window_left: int, window_right: int, scale: float | None = None, out=None, lse=None):
+    """bf16 sliding-window forward: key j visible to query i iff i-left <= j <= i+right
+    (negative = unlimited); returns ``(o, lse)``."""
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,N,d]")
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _fwd_outputs(q, out, lse)
+    st = lib.fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                           float(scale), int(window_left), int(window_right), _stream())
+    if st != 0:
+        raise FAError(st, "fa_fwd_window")
+    return out, lse
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """bf16 block-sparse forward over 64 x 64 blocks; ``block_mask`` is a uint8 GPU tensor
+    ``[H, nb, nb]`` or ``[nb, nb]`` (shared by all heads), nb = ceil(N/64); returns ``(o, lse)``."""
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,N,d]")
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    nb = (N + 63) // 64
+    if block_mask.dim() == 3:
+        _check(block_mask, "block_mask", torch.uint8, (H, nb, nb))
+        per_head = 1
+    else:
+        _check(block_mask, "block_mask", torch.uint8, (nb, nb))
+        per_head = 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _fwd_outputs(q, out, lse)
+    st = lib.fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
+                                d, float(scale), int(bool(causal)), block_mask.data_ptr(), per_head, _stream())
+    if st != 0:
+        raise FAError(st, "fa_fwd_blocksparse")
     return out, lse

@@ -181,7 +181,8 @@ def _graph_ms(fn, calls: int, warmup: int = 3) -> float:
 
 def next_rows():
     """Key-split forward (fa_fwd_splitkv) against fa_fwd on grids too small to fill
-    the GPU, and the Eq. (2) merge kernel (fa_lse_merge) against the HBM roof."""
+    the GPU, the sliding-window and block-sparse forwards, and the Eq. (2) merge
+    kernel (fa_lse_merge) against the HBM roof."""
     res = {}
     for name, (B, H, N, d, causal) in {"B1H8N2048d128": (1, 8, 2048, 128, False),
                                        "B1H4N4096d128_causal": (1, 4, 4096, 128, True),
@@ -198,6 +199,30 @@ def next_rows():
         res[name] = {"parts": parts, "fa_fwd_ms": round(t_f, 5), "fa_fwd_splitkv_ms": round(t_s, 5),
                      "speedup": round(t_f / t_s, 3), "splitkv_tflops": round(flop / (t_s * 1e-3) / 1e12, 1),
                      "splitkv_frac_peak": round(flop / (t_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    # tile-skipping masks at the benchmark shape: FLOP counted on the visible (query, key) pairs only
+    B, H, N, d = 1, 8, 16384, 128
+    q, k, v = (t.cuda() for t in make_inputs(B, H, N, d, "bf16", 9, 1.0))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    t_d = _graph_ms(lambda: fa.fwd(q, k, v, out=o, lse=lse), 5)
+    pairs = sum(min(N - 1, i + 512) - max(0, i - 512) + 1 for i in range(N))
+    t_w = _graph_ms(lambda: fa.fwd_window(q, k, v, 512, 512, out=o, lse=lse), 10)
+    fl_w = 4 * B * H * pairs * d
+    res["window_512_512_B1H8N16384d128"] = {
+        "ms": round(t_w, 5), "visible_fraction": round(pairs / N / N, 4), "dense_fa_fwd_ms": round(t_d, 5),
+        "tflops_visible": round(fl_w / (t_w * 1e-3) / 1e12, 1),
+        "frac_peak": round(fl_w / (t_w * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    nb = N // 64
+    g = torch.Generator().manual_seed(9)
+    bm = (torch.rand((nb, nb), generator=g) < 0.5).to(torch.uint8)
+    kept = int(bm.sum())
+    bmd = bm.cuda()
+    t_b = _graph_ms(lambda: fa.fwd_blocksparse(q, k, v, bmd, out=o, lse=lse), 5)
+    fl_b = 4 * B * H * kept * 64 * 64 * d
+    res["blocksparse_half_B1H8N16384d128"] = {
+        "ms": round(t_b, 5), "kept_blocks": round(kept / nb / nb, 4), "dense_fa_fwd_ms": round(t_d, 5),
+        "tflops_visible": round(fl_b / (t_b * 1e-3) / 1e12, 1),
+        "frac_peak": round(fl_b / (t_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     # merge kernel alone: S = 4 parts of B1 H8 N2048 d128
     S, B, H, N, d = 4, 1, 8, 2048, 128
     g = torch.Generator().manual_seed(9)

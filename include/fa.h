@@ -173,6 +173,39 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 int fa_lse_merge(const float* o_parts, const float* lse_parts, int num_parts, void* o, float* lse,
                  int B, int H, int N, int d, hipStream_t stream);
 
+/*
+ * fa_fwd_window - bf16 forward attention restricted to a sliding window:
+ * key j is visible to query i iff i - window_left <= j <= i + window_right,
+ * where a negative bound means no limit on that side ((-1, -1) is fa_fwd
+ * without a mask, (-1, 0) is fa_fwd with causal = 1, (512, 512) is the
+ * window of the FlashAttention-2 principle and deployment page's SDPA
+ * example).  Every query sees at least itself.  Inputs, outputs (o, lse) and
+ * conventions as fa_fwd; key tiles outside every row's window are skipped.
+ * Errors: as fa_fwd (without the causal flag).
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int N, int d, float scale, int window_left, int window_right,
+                  hipStream_t stream);
+
+/*
+ * fa_fwd_blocksparse - bf16 forward attention over the kept blocks of a
+ * block-sparse mask (block-sparse FlashAttention: FlashAttention
+ * optimisation page, section 7).  The N x N score matrix is cut into 64 x 64
+ * blocks; block_mask[h][i/64][j/64] != 0 keeps the block containing (i, j),
+ * 0 drops it.  block_mask: device pointer to unsigned char
+ * [H][nb][nb] (mask_per_head = 1) or [nb][nb] shared by every head
+ * (mask_per_head = 0), nb = ceil(N / 64), any alignment, read only.  With
+ * causal = 1 the causal mask applies on top.  Dropped blocks cost neither
+ * loads nor MFMAs.  A row that sees no key gets o = 0 and lse = -inf.
+ * Other inputs, outputs and conventions as fa_fwd.
+ * Preconditions beyond fa_fwd's: N <= 65536 (FA_ERR_SHAPE), mask_per_head in
+ * {0, 1} (FA_ERR_ARG), block_mask not NULL (FA_ERR_NULL) and not
+ * overlapping o or lse (FA_ERR_ARG).
+ */
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, float scale, int causal,
+                       const unsigned char* block_mask, int mask_per_head, hipStream_t stream);
+
 /* fa_status_string - static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

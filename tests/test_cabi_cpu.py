@@ -39,7 +39,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_bytes", "fa_bwd",
                                            "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_bytes",
-                                           "fa_fwd_splitkv", "fa_lse_merge", "fa_status_string"])
+                                           "fa_fwd_splitkv", "fa_lse_merge", "fa_fwd_window",
+                                           "fa_fwd_blocksparse", "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -197,6 +198,25 @@ def test_lse_merge_validation(lib):
     assert f(op.ptr, lp.ptr, S, o.ptr, o.ptr, B, H, N, d, None) == ST["ARG"]        # lse over o
 
 
+def test_mask_validation(lib):
+    B, H, N, d = 1, 2, 130, 64
+    bufs = [_Buf(B * H * N * d * 2) for _ in range(4)] + [_Buf(B * H * N * 4)]
+    q, k, v, o, l = [b.ptr for b in bufs]
+    fw = lib.fa_fwd_window
+    assert fw(None, k, v, o, l, B, H, N, d, 0.125, 4, 4, None) == ST["NULL"]
+    assert fw(q, k, v, o, l, B, H, N, 80, 0.125, 4, 4, None) == ST["HEAD_DIM"]
+    assert fw(q, k, v, o, l, B, H, N, d, -1.0, 4, 4, None) == ST["SCALE"]
+    assert fw(q, k, v, q, l, B, H, N, d, 0.125, 4, 4, None) == ST["ARG"]
+    nb = 3
+    m = _Buf(H * nb * nb)
+    fb = lib.fa_fwd_blocksparse
+    assert fb(q, k, v, o, l, B, H, N, d, 0.125, 0, None, 1, None) == ST["NULL"]
+    assert fb(q, k, v, o, l, B, H, 65537, d, 0.125, 0, m.ptr, 1, None) == ST["SHAPE"]
+    assert fb(q, k, v, o, l, B, H, N, d, 0.125, 2, m.ptr, 1, None) == ST["ARG"]
+    assert fb(q, k, v, o, l, B, H, N, d, 0.125, 0, m.ptr, 2, None) == ST["ARG"]
+    assert fb(q, k, v, o, l, B, H, N, d, 0.125, 0, o, 1, None) == ST["ARG"]      # mask overlaps the output
+
+
 def test_validate_header_with_gxx(tmp_path):
     """Host unit test of fa_validate.h compiled by g++ (no HIP, no GPU)."""
     src = tmp_path / "t.cpp"
@@ -251,6 +271,11 @@ int main() {
   EXPECT(validate_lse_merge(mem[0], mem[1], 2, mem[2], mem[3], Shape{1, 1, 8, 64}) == kOk);
   EXPECT(validate_lse_merge(mem[0], mem[1], 0, mem[2], mem[3], Shape{1, 1, 8, 64}) == kErrArg);
   EXPECT(validate_lse_merge(mem[0], mem[1], 2, mem[0] + 64, mem[3], Shape{1, 1, 8, 64}) == kErrArg);
+  EXPECT(block_mask_bytes(Shape{1, 3, 130, 64}, 1) == 27 && block_mask_bytes(Shape{1, 3, 130, 64}, 0) == 9);
+  EXPECT(validate_fwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 1, mem[5], 1) == kOk);
+  EXPECT(validate_fwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 1, nullptr, 1) == kErrNull);
+  EXPECT(validate_fwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 1, mem[3], 1) == kErrArg);
+  EXPECT(validate_fwd_window(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f) == kOk);
   return fails ? 1 : 0;
 }
 ''')
