@@ -12,6 +12,11 @@
 namespace fa {
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
                            int d, float scale, int causal, hipStream_t st);
+hipError_t launch_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                           int d, float scale, int causal, hipStream_t st);
+hipError_t launch_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                           int causal, void* ws, hipStream_t st);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                           int N, int d, float scale, int causal, hipStream_t st);
 hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -72,6 +77,31 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   if (st != fa::kOk) return st;
   return fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream) == hipSuccess ? fa::kOk
                                                                                               : fa::kErrHip;
+}
+
+int fa_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                float scale, int causal, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_fwd(q, k, v, o, lse, s, scale, causal, 2);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_fwd_fp16(q, k, v, o, lse, B, H, N, d, scale, causal, stream) == hipSuccess ? fa::kOk
+                                                                                               : fa::kErrHip;
+}
+
+int fa_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, workspace, workspace_bytes);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_bwd_fp16(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, workspace, stream) ==
+                 hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) { return fa::bwd_workspace_bytes(fa::Shape{B, H, N, d}); }

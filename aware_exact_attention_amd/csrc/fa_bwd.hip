@@ -51,10 +51,12 @@ __device__ __forceinline__ int tr_off(int b, int r2, int lane) {
   return row * (2 * DD) + (((col >> 3) ^ tile_swz<DD>(row)) * 16) + (col & 7) * 2;
 }
 
-__device__ __forceinline__ bf16x8 tr_pair(const char* base, int off0, int off1) {
+template <typename E>
+__device__ __forceinline__ typename Vec<E>::v8 tr_pair(const char* base, int off0, int off1) {
   typedef __attribute__((address_space(3))) short4_t* lds_s4;
-  const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + off0)));
-  const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + off1)));
+  using v4 = typename Vec<E>::v4;
+  const v4 lo = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + off0)));
+  const v4 hi = __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(base + off1)));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -78,22 +80,23 @@ __device__ __forceinline__ int swz_src(int p) {
 // ---------------------------------------------------------------------------
 // 1. D = rowsum(dO * O) and LSE2 = LSE * log2(e).  8 lanes per row.
 // ---------------------------------------------------------------------------
-template <int D>
+template <typename E, int D>
 __global__ void __launch_bounds__(256)
-bwd_pre_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
+bwd_pre_kernel(const E* __restrict__ O, const E* __restrict__ dO, const float* __restrict__ LSE,
                float* __restrict__ Dv, float* __restrict__ lse2, long long rows) {
+  using v8 = typename Vec<E>::v8;
   constexpr int PER = D / 8;  // elements per lane
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gid >> 3;
   const int sub = threadIdx.x & 7;
   float acc = 0.f;
   if (row < rows) {
-    const __bf16* o = O + row * D + sub * PER;
-    const __bf16* g = dO + row * D + sub * PER;
+    const E* o = O + row * D + sub * PER;
+    const E* g = dO + row * D + sub * PER;
 #pragma unroll
     for (int u = 0; u < PER / 8; ++u) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + 8 * u);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(g + 8 * u);
+      const v8 a = *reinterpret_cast<const v8*>(o + 8 * u);
+      const v8 b = *reinterpret_cast<const v8*>(g + 8 * u);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
     }
@@ -144,13 +147,14 @@ struct DkdvTile {
   static_assert(QT % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
 
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 1)
-bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
-                __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int Tk, float c /* scale*log2(e) */,
+bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+                const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
+                E* __restrict__ dK, E* __restrict__ dV, int N, int Tk, float c /* scale*log2(e) */,
                 float scale) {
   using T = DkdvTile<D>;
+  using v8 = typename Vec<E>::v8;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
 
   const int tid = threadIdx.x;
@@ -172,12 +176,12 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
   // Keys past N read as zero; their dK and dV rows are never stored.
   const int kw0 = k0 + pair * 32;
   const int key = kw0 + l32;
-  bf16x8 kv[T::KS];
+  v8 kv[T::KS];
   {
     const __amdgpu_buffer_rsrc_t r = make_rsrc((role_a ? K : V) + head, head_bytes);
 #pragma unroll
     for (int st = 0; st < T::KS; ++st)
-      kv[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, key * T::RS + (16 * st + 8 * half) * 2, 0, 0));
+      kv[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(r, key * T::RS + (16 * st + 8 * half) * 2, 0, 0));
   }
 
   // Direct-to-LDS loads of the Q and dO tiles of a step: load u of this wave
@@ -243,16 +247,16 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
 #pragma unroll
     for (int qb = 0; qb < T::QB; ++qb) acc1[qb] = f32x16{};
     {
-      bf16x8 a[T::QB];
+      v8 a[T::QB];
 #pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb) a[qb] = *reinterpret_cast<const bf16x8*>(sb + qb * 32 * T::RS + rof[0]);
+      for (int qb = 0; qb < T::QB; ++qb) a[qb] = *reinterpret_cast<const v8*>(sb + qb * 32 * T::RS + rof[0]);
 #pragma unroll
       for (int st = 0; st < T::KS; ++st) {
-        bf16x8 an[T::QB];
+        v8 an[T::QB];
         if (st + 1 < T::KS) {
 #pragma unroll
           for (int qb = 0; qb < T::QB; ++qb)
-            an[qb] = *reinterpret_cast<const bf16x8*>(sb + qb * 32 * T::RS + rof[st + 1]);
+            an[qb] = *reinterpret_cast<const v8*>(sb + qb * 32 * T::RS + rof[st + 1]);
         }
 #pragma unroll
         for (int qb = 0; qb < T::QB; ++qb) acc1[qb] = mfma32(a[qb], kv[st], acc1[qb]);
@@ -264,8 +268,8 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     }
 
     // ---- A: P = exp2(S*c - LSE2) (causal: keys after the query -> 0), to
-    // its partner through LDS and rounded to bf16 for dV
-    bf16x8 op[T::PS];  // P (A) or dS (B), bf16, MFMA B operand of the second product
+    // its partner through LDS and rounded to the input type for dV
+    v8 op[T::PS];  // P (A) or dS (B), 16-bit, MFMA B operand of the second product
     if (role_a) {
       // only the first two steps of a causal key block straddle the diagonal
       const bool need = CAUSAL && (i - i0 < 2);
@@ -281,13 +285,13 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
             if (need && key > qs + qb * 32 + 8 * g + 4 * half + e) p = 0.f;
             p4[e] = p;
             const int j = 4 * g + e;
-            op[qb * 2 + (j >> 3)][j & 7] = (__bf16)p;
+            op[qb * 2 + (j >> 3)][j & 7] = (E)p;
           }
           *reinterpret_cast<f32x4*>(xp + (qb * 4 + g) * 64 * 16) = p4;
         }
     }
     __syncthreads();  // P of this step is in LDS
-    // ---- B: dS = P * (dP - D), rounded to bf16
+    // ---- B: dS = P * (dP - D), rounded to the input type
     if (!role_a) {
 #pragma unroll
       for (int qb = 0; qb < T::QB; ++qb)
@@ -298,7 +302,7 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * g + e;
-            op[qb * 2 + (j >> 3)][j & 7] = (__bf16)(p4[e] * (acc1[qb][j] - d4[e]));
+            op[qb * 2 + (j >> 3)][j & 7] = (E)(p4[e] * (acc1[qb][j] - d4[e]));
           }
         }
     }
@@ -306,15 +310,15 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
     // ---- second product: dV^T += dO^T P (A) or dK^T += Q^T dS (B), k = query
     // in the accumulator's order; transposed operands read one MFMA ahead
     {
-      bf16x8 a = tr_pair(sb, tof[0][0], tof[0][1]);
+      v8 a = tr_pair<E>(sb, tof[0][0], tof[0][1]);
 #pragma unroll
       for (int ps = 0; ps < T::PS; ++ps)
 #pragma unroll
         for (int b = 0; b < T::DB; ++b) {
           const int nb = (b + 1 < T::DB) ? b + 1 : 0;
           const int nps = (b + 1 < T::DB) ? ps : ps + 1;
-          bf16x8 an;
-          if (nps < T::PS) an = tr_pair(sb + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
+          v8 an;
+          if (nps < T::PS) an = tr_pair<E>(sb + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
           acc2[b] = mfma32(a, op[ps], acc2[b]);
           if (nps < T::PS) a = an;
         }
@@ -335,8 +339,8 @@ bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, cons
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w;
-      w[0] = pack_bf16x2(acc2[b][4 * g + 0] * f, acc2[b][4 * g + 1] * f);
-      w[1] = pack_bf16x2(acc2[b][4 * g + 2] * f, acc2[b][4 * g + 3] * f);
+      w[0] = pack2<E>(acc2[b][4 * g + 0] * f, acc2[b][4 * g + 1] * f);
+      w[1] = pack2<E>(acc2[b][4 * g + 2] * f, acc2[b][4 * g + 3] * f);
       __builtin_amdgcn_raw_buffer_store_b64(w, ro, key * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
 }
@@ -361,12 +365,13 @@ struct DqTile {
   static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
 
-template <int D, bool CAUSAL, int NW>
+template <typename E, int D, bool CAUSAL, int NW>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
-bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-              const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
-              __bf16* __restrict__ dQ, int N, int Tr, float c /* scale*log2(e) */, float scale) {
+bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+              const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
+              E* __restrict__ dQ, int N, int Tr, float c /* scale*log2(e) */, float scale) {
   using T = DqTile<D, NW>;
+  using v8 = typename Vec<E>::v8;
   __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
 
   const int tid = threadIdx.x;
@@ -380,23 +385,23 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
   if (CAUSAL) it = Tr - 1 - it;  // longest rows first
   const int q0 = it * T::BR;
   const size_t head = size_t(bh) * N * D;
-  const __bf16* Kh = K + head;
-  const __bf16* Vh = V + head;
+  const E* Kh = K + head;
+  const E* Vh = V + head;
   const int head_bytes = N * T::RS;
 
   // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): row
   // qrow, columns 16*s + 8*half .. +7.  Rows past N read as zero.
   const int wq0 = q0 + wave * 32;
   const int qrow = wq0 + l32;
-  bf16x8 qf[T::KS], df[T::KS];
+  v8 qf[T::KS], df[T::KS];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head, head_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(dO + head, head_bytes);
 #pragma unroll
     for (int s = 0; s < T::KS; ++s) {
       const int off = qrow * T::RS + (16 * s + 8 * half) * 2;
-      qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-      df[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
+      qf[s] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      df[s] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
     }
   }
   // this lane's query: LSE in base 2 and D (rows past N: 0; their dQ is never stored)
@@ -457,9 +462,9 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
       // scheduling barriers (left alone, the scheduler pulls each read next to
       // its MFMA and the LDS latency shows)
       constexpr int KPF = 2;
-      bf16x8 ka[KPF][T::KB], va[KPF][T::KB];
+      v8 ka[KPF][T::KB], va[KPF][T::KB];
       auto rd = [&](int st, int kb, int v) {
-        return *reinterpret_cast<const bf16x8*>(base + v * T::TILE + kb * 32 * T::RS + rof[st]);
+        return *reinterpret_cast<const v8*>(base + v * T::TILE + kb * 32 * T::RS + rof[st]);
       };
 #pragma unroll
       for (int st = 0; st < KPF; ++st)
@@ -489,30 +494,30 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
         if (st + KPF < T::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::KB, 0);
       }
     }
-    // ---- dS^T = P^T * (dP^T - D) with P^T = exp2(S^T*c - LSE2), rounded to bf16.
+    // ---- dS^T = P^T * (dP^T - D) with P^T = exp2(S^T*c - LSE2), rounded to the input type.
     // Keys past N have zero K and V rows, so they add nothing to dQ; causal
     // keys after the query are masked on the tiles that straddle the diagonal.
     const int key0 = j * T::BC;
     const bool need = CAUSAL && (key0 + T::BC - 1 > wq0);
-    bf16x8 db[T::PS];
+    v8 db[T::PS];
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pr = exp2_fast(fmaf(s[kb][r], c, -lq));
         if (need && key0 + kb * 32 + acc_row(r, lane) > qrow) pr = 0.f;
-        db[kb * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (p[kb][r] - dd));
+        db[kb * 2 + (r >> 3)][r & 7] = (E)(pr * (p[kb][r] - dd));
       }
     // ---- dQ^T += K_j^T dS^T (k = key, in the accumulator's order)
-    bf16x8 ka = tr_pair(base, tof[0][0], tof[0][1]);
+    v8 ka = tr_pair<E>(base, tof[0][0], tof[0][1]);
 #pragma unroll
     for (int ps = 0; ps < T::PS; ++ps)
 #pragma unroll
       for (int b = 0; b < T::DB; ++b) {
         const int nb = (b + 1 < T::DB) ? b + 1 : 0;
         const int nps = (b + 1 < T::DB) ? ps : ps + 1;
-        bf16x8 kn;
-        if (nps < T::PS) kn = tr_pair(base + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
+        v8 kn;
+        if (nps < T::PS) kn = tr_pair<E>(base + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
         acc[b] = mfma32(ka, db[ps], acc[b]);
         if (nps < T::PS) ka = kn;
       }
@@ -543,8 +548,8 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w;
-      w[0] = pack_bf16x2(acc[b][4 * g + 0] * scale, acc[b][4 * g + 1] * scale);
-      w[1] = pack_bf16x2(acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
+      w[0] = pack2<E>(acc[b][4 * g + 0] * scale, acc[b][4 * g + 1] * scale);
+      w[1] = pack2<E>(acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
       __builtin_amdgcn_raw_buffer_store_b64(w, ro, qrow * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
 }
@@ -552,7 +557,7 @@ bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const 
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
                                void* ws, hipStream_t st) {
@@ -564,8 +569,8 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   const float c = scale * kLog2e;
 
   const long long pre_blocks = (rows * 8 + 255) / 256;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, st,
-                     (const __bf16*)o, (const __bf16*)dO, lse, Dv, lse2, rows);
+  hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((unsigned)pre_blocks), dim3(256), 0, st,
+                     (const E*)o, (const E*)dO, lse, Dv, lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -579,30 +584,43 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   const int Tr = dq8 ? (N + DqTile<D, 8>::BR - 1) / DqTile<D, 8>::BR : (N + DqTile<D, 4>::BR - 1) / DqTile<D, 4>::BR;
   const long long Gq = (long long)B * H * Tr;
   if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                     (const float*)lse2, (const float*)Dv, (__bf16*)dk, (__bf16*)dv, N, Tk, c, scale);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
+                     (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
+                     (const float*)lse2, (const float*)Dv, (E*)dk, (E*)dv, N, Tk, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dq8)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 8>), dim3((unsigned)Gq), dim3(DqTile<D, 8>::NT), 0, st,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       (const float*)lse2, (const float*)Dv, (__bf16*)dq, N, Tr, c, scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 8>), dim3((unsigned)Gq), dim3(DqTile<D, 8>::NT), 0, st,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
+                       (const float*)lse2, (const float*)Dv, (E*)dq, N, Tr, c, scale);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 4>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT), 0, st,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dO,
-                       (const float*)lse2, (const float*)Dv, (__bf16*)dq, N, Tr, c, scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 4>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT), 0, st,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
+                       (const float*)lse2, (const float*)Dv, (E*)dq, N, Tr, c, scale);
   return hipGetLastError();
+}
+
+template <typename E>
+static hipError_t launch_bwd_e(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                               int causal, void* ws, hipStream_t st) {
+  if (d == 128)
+    return causal ? launch_bwd_t<E, 128, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st)
+                  : launch_bwd_t<E, 128, false>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st);
+  return causal ? launch_bwd_t<E, 64, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st)
+                : launch_bwd_t<E, 64, false>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st);
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                       int causal, void* ws, hipStream_t st) {
-  if (d == 128)
-    return causal ? launch_bwd_t<128, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st)
-                  : launch_bwd_t<128, false>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st);
-  return causal ? launch_bwd_t<64, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st)
-                : launch_bwd_t<64, false>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st);
+  return launch_bwd_e<__bf16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, ws, st);
+}
+
+hipError_t launch_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                           int causal, void* ws, hipStream_t st) {
+  return launch_bwd_e<_Float16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, ws, st);
 }
 
 }  // namespace fa

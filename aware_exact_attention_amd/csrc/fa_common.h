@@ -9,6 +9,8 @@ namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -30,6 +32,24 @@ constexpr long long kNumCUs = 256;
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// v_mfma_f32_32x32x16_f16: the same shape and lane layout for fp16 operands.
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Vector types of a 16-bit element type (__bf16 or _Float16).
+template <typename E>
+struct Vec;
+template <>
+struct Vec<__bf16> {
+  using v8 = bf16x8;
+  using v4 = bf16x4;
+};
+template <>
+struct Vec<_Float16> {
+  using v8 = f16x8;
+  using v4 = f16x4;
+};
 
 // Row index (within a 32x32 accumulator block) held by element j of lane l.
 __device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
@@ -95,6 +115,16 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, 
 // Pack two fp32 values into two bf16 (round to nearest even) in one dword.
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  unsigned short ua = __builtin_bit_cast(unsigned short, a);
+  unsigned short ub = __builtin_bit_cast(unsigned short, b);
+  return unsigned(ua) | (unsigned(ub) << 16);
+}
+
+// Pack two fp32 values into two 16-bit values of type E (round to nearest
+// even) in one dword.
+template <typename E>
+__device__ __forceinline__ unsigned pack2(float lo, float hi) {
+  E a = (E)lo, b = (E)hi;
   unsigned short ua = __builtin_bit_cast(unsigned short, a);
   unsigned short ub = __builtin_bit_cast(unsigned short, b);
   return unsigned(ua) | (unsigned(ub) << 16);

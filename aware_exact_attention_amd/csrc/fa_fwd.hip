@@ -80,12 +80,13 @@ struct MaskArgs {
   int nb, H;
 };
 
-template <int D, bool CAUSAL, int NW, bool SPLIT, int MODE>
+template <typename E, int D, bool CAUSAL, int NW, bool SPLIT, int MODE>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
-fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-                int N, int Tr, float c, SplitArgs sp, MaskArgs mk) {
+fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V, E* __restrict__ O,
+           float* __restrict__ LSE, int N, int Tr, float c, SplitArgs sp, MaskArgs mk) {
   using T = FwdTile<D, NW>;
+  using v8 = typename Vec<E>::v8;
+  using v4 = typename Vec<E>::v4;
   constexpr bool WINDOW = MODE == kMaskWindow, BLOCKS = MODE == kMaskBlocks;
   static_assert(!(SPLIT && MODE != kMaskDense), "key split only with the dense or causal mask");
   static_assert(!BLOCKS || (T::BC == kMaskBlock && T::BR == 2 * kMaskBlock), "mask blocks are key tiles and half a row block");
@@ -107,20 +108,20 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if (CAUSAL) it = Tr - 1 - it;  // longest rows first
   const int q0 = it * T::BR;
   const size_t head = size_t(bh) * N * D;
-  const __bf16* Kh = K + head;
-  const __bf16* Vh = V + head;
+  const E* Kh = K + head;
+  const E* Vh = V + head;
   const int head_bytes = N * T::RS;
 
   // Q fragment (B operand of S^T = K Q^T): row qrow, columns 16*s + 8*half .. +7.
   // Rows past N read as zero (buffer bounds).
   const int wq0 = q0 + wave * 32;
   const int qrow = wq0 + l32;
-  bf16x8 qf[T::KS];
+  v8 qf[T::KS];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head, head_bytes);
 #pragma unroll
     for (int s = 0; s < T::KS; ++s)
-      qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+      qf[s] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(
                                              rq, qrow * T::RS + (16 * s + 8 * half) * 2, 0, 0));
   }
 
@@ -233,19 +234,19 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // the scheduler pulls each read next to its MFMA and the LDS latency shows)
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     constexpr int KPF = 2;
-    bf16x8 kr[KPF][2];
+    v8 kr[KPF][2];
 #pragma unroll
     for (int st = 0; st < KPF; ++st) {
-      kr[st][0] = *reinterpret_cast<const bf16x8*>(base + kof[st]);
-      kr[st][1] = *reinterpret_cast<const bf16x8*>(base + kof[st] + 32 * T::RS);
+      kr[st][0] = *reinterpret_cast<const v8*>(base + kof[st]);
+      kr[st][1] = *reinterpret_cast<const v8*>(base + kof[st] + 32 * T::RS);
     }
 #pragma unroll
     for (int st = 0; st < T::KS; ++st) {
       s0 = mfma32(kr[st % KPF][0], qf[st], s0);
       s1 = mfma32(kr[st % KPF][1], qf[st], s1);
       if (st + KPF < T::KS) {
-        kr[st % KPF][0] = *reinterpret_cast<const bf16x8*>(base + kof[st + KPF]);
-        kr[st % KPF][1] = *reinterpret_cast<const bf16x8*>(base + kof[st + KPF] + 32 * T::RS);
+        kr[st % KPF][0] = *reinterpret_cast<const v8*>(base + kof[st + KPF]);
+        kr[st % KPF][1] = *reinterpret_cast<const v8*>(base + kof[st + KPF] + 32 * T::RS);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * KPF, 0);
@@ -298,7 +299,7 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int b = 0; b < T::DB; ++b) o[b] *= alpha;
     }
     // P, rounded to bf16 for the PV product; l sums the fp32 values
-    bf16x8 pb[T::PS];
+    v8 pb[T::PS];
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
@@ -306,22 +307,22 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_fast(fmaf(s[kb][r], c, -mu));
         rs += p;
-        pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
+        pb[kb * 2 + (r >> 3)][r & 7] = (E)p;
       }
     l += rs;
     // ---- O^T += V_j^T P^T: DB independent chains; V^T operands come from two
     // transposing reads of the row-major V tile, VPF operands ahead
     auto vread = [&](int b, int ps) {
       const char* vb = base + ps * 16 * T::RS;
-      const bf16x4 lo = __builtin_bit_cast(
-          bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(vb + vof[b][0])));
-      const bf16x4 hi = __builtin_bit_cast(
-          bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(vb + vof[b][1])));
+      const v4 lo = __builtin_bit_cast(
+          v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(vb + vof[b][0])));
+      const v4 hi = __builtin_bit_cast(
+          v4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(vb + vof[b][1])));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     constexpr int VPF = 3;  // V operands in flight, in (ps, b) order
     constexpr int NV = T::PS * T::DB;
-    bf16x8 vr[VPF];
+    v8 vr[VPF];
 #pragma unroll
     for (int u = 0; u < VPF; ++u) vr[u] = vread(u % T::DB, u / T::DB);
 #pragma unroll
@@ -381,8 +382,8 @@ fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w;
-      w[0] = pack_bf16x2(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv);
-      w[1] = pack_bf16x2(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
+      w[0] = pack2<E>(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv);
+      w[1] = pack2<E>(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
       __builtin_amdgcn_raw_buffer_store_b64(w, ro, qrow * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
   if (half == 0 && qrow < N) LSE[size_t(bh) * N + qrow] = (!BLOCKS || lt > 0.f) ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
@@ -486,16 +487,16 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int NW>
-static hipError_t launch_fwd_bf16_nw(const void* q, const void* k, const void* v, void* o, float* lse,
-                                     int B, int H, int N, float scale, hipStream_t st) {
+template <typename E, int D, bool CAUSAL, int NW>
+static hipError_t launch_fwd_nw(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                int N, float scale, hipStream_t st) {
   using T = FwdTile<D, NW>;
   const int Tr = (N + T::BR - 1) / T::BR;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, false, kMaskDense>), dim3((unsigned)G), dim3(T::NT), 0, st,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
-                     scale * kLog2e, SplitArgs{1, 0, nullptr, nullptr, 0, 0}, MaskArgs{});
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, NW, false, kMaskDense>), dim3((unsigned)G), dim3(T::NT), 0, st,
+                     (const E*)q, (const E*)k, (const E*)v, (E*)o, lse, N, Tr, scale * kLog2e,
+                     SplitArgs{1, 0, nullptr, nullptr, 0, 0}, MaskArgs{});
   return hipGetLastError();
 }
 
@@ -505,20 +506,31 @@ static hipError_t launch_fwd_bf16_nw(const void* q, const void* k, const void* v
 // covers every CU.  Causal launches keep 128-row tiles (their per-tile work is
 // uneven and finer tiles balance it better), and so does d = 64, whose tiles
 // carry half the MFMA work per barrier (measured slower with 8 waves).
-template <int D, bool CAUSAL>
-static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                                    int B, int H, int N, float scale, hipStream_t st) {
+template <typename E, int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                               int N, float scale, hipStream_t st) {
   const long long G8 = (long long)B * H * ((N + FwdTile<D, 8>::BR - 1) / FwdTile<D, 8>::BR);
-  if (D == 128 && !CAUSAL && G8 >= kNumCUs) return launch_fwd_bf16_nw<D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, st);
-  return launch_fwd_bf16_nw<D, CAUSAL, 4>(q, k, v, o, lse, B, H, N, scale, st);
+  if (D == 128 && !CAUSAL && G8 >= kNumCUs) return launch_fwd_nw<E, D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, st);
+  return launch_fwd_nw<E, D, CAUSAL, 4>(q, k, v, o, lse, B, H, N, scale, st);
+}
+
+template <typename E>
+static hipError_t launch_fwd_e(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                               int N, int d, float scale, int causal, hipStream_t st) {
+  if (d == 128) return causal ? launch_fwd_t<E, 128, true>(q, k, v, o, lse, B, H, N, scale, st)
+                              : launch_fwd_t<E, 128, false>(q, k, v, o, lse, B, H, N, scale, st);
+  return causal ? launch_fwd_t<E, 64, true>(q, k, v, o, lse, B, H, N, scale, st)
+                : launch_fwd_t<E, 64, false>(q, k, v, o, lse, B, H, N, scale, st);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, int causal, hipStream_t st) {
-  if (d == 128) return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, B, H, N, scale, st)
-                              : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, B, H, N, scale, st);
-  return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, B, H, N, scale, st)
-                : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, B, H, N, scale, st);
+  return launch_fwd_e<__bf16>(q, k, v, o, lse, B, H, N, d, scale, causal, st);
+}
+
+hipError_t launch_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, int d, float scale, int causal, hipStream_t st) {
+  return launch_fwd_e<_Float16>(q, k, v, o, lse, B, H, N, d, scale, causal, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -604,7 +616,7 @@ hipError_t launch_lse_merge(const float* op, const float* lp, int S, void* o, fl
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                      int H, int N, float scale, int S, void* ws, hipStream_t st) {
-  if (S <= 1) return launch_fwd_bf16_t<D, CAUSAL>(q, k, v, o, lse, B, H, N, scale, st);
+  if (S <= 1) return launch_fwd_t<__bf16, D, CAUSAL>(q, k, v, o, lse, B, H, N, scale, st);
   using T = FwdTile<D, 4>;
   const SplitLayout w = split_workspace_layout(Shape{B, H, N, D}, S);
   const int Tr = (N + T::BR - 1) / T::BR;
@@ -614,7 +626,7 @@ static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v
   char* base = reinterpret_cast<char*>(ws);
   SplitArgs sp{S, (Tc + S - 1) / S, reinterpret_cast<float*>(base + w.o_parts),
                reinterpret_cast<float*>(base + w.lse_parts), (long long)B * H * N * D, (long long)B * H * N};
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, true, kMaskDense>), dim3((unsigned)G), dim3(T::NT), 0, st,
+  hipLaunchKernelGGL((fwd_kernel<__bf16, D, CAUSAL, 4, true, kMaskDense>), dim3((unsigned)G), dim3(T::NT), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
                      scale * kLog2e, sp, MaskArgs{});
   hipError_t e = hipGetLastError();
@@ -639,7 +651,7 @@ static hipError_t launch_fwd_masked_t(const void* q, const void* k, const void* 
   const int Tr = (N + T::BR - 1) / T::BR;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, false, MODE>), dim3((unsigned)G), dim3(T::NT), 0, st,
+  hipLaunchKernelGGL((fwd_kernel<__bf16, D, CAUSAL, 4, false, MODE>), dim3((unsigned)G), dim3(T::NT), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
                      scale * kLog2e, SplitArgs{1, 0, nullptr, nullptr, 0, 0}, mk);
   return hipGetLastError();

@@ -24,6 +24,9 @@ _c_int, _c_float, _c_size_t, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp]),
     "fa_fwd_f32": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp]),
+    "fa_fwd_fp16": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp]),
+    "fa_bwd_fp16": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
+                             _c_int, _vp, _c_size_t, _vp]),
     "fa_bwd_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "fa_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
                         _c_int, _vp, _c_size_t, _vp]),
@@ -90,7 +93,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
     """Forward attention of ``[B,H,N,d]`` tensors; returns ``(o, lse)``.
 
-    bf16 inputs run ``fa_fwd``; float32 inputs run ``fa_fwd_f32``.  ``scale``
+    bf16 inputs run ``fa_fwd``, float16 ``fa_fwd_fp16``, float32 ``fa_fwd_f32``.  ``scale``
     defaults to ``1/sqrt(d)``.  ``out``/``lse`` may be passed preallocated.
     """
     lib = load()
@@ -98,7 +101,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         raise ValueError("q must be [B,H,N,d]")
     B, H, N, d = q.shape
     dtype = q.dtype
-    if dtype not in (torch.bfloat16, torch.float32):
+    if dtype not in (torch.bfloat16, torch.float16, torch.float32):
         raise TypeError(f"unsupported dtype {dtype}")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, dtype, (B, H, N, d))
@@ -112,11 +115,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
         _check(lse, "lse", torch.float32, (B, H, N))
-    fn = lib.fa_fwd if dtype == torch.bfloat16 else lib.fa_fwd_f32
-    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-            float(scale), int(bool(causal)), _stream())
+    name = {torch.bfloat16: "fa_fwd", torch.float16: "fa_fwd_fp16", torch.float32: "fa_fwd_f32"}[dtype]
+    st = getattr(lib, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                            float(scale), int(bool(causal)), _stream())
     if st != 0:
-        raise FAError(st, "fa_fwd" if dtype == torch.bfloat16 else "fa_fwd_f32")
+        raise FAError(st, name)
     return out, lse
 
 
@@ -125,7 +128,7 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 
 def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, workspace=None, out=None):
-    """Backward attention (bf16); returns ``(dq, dk, dv)``.
+    """Backward attention (bf16 or float16, ``fa_bwd`` / ``fa_bwd_fp16``); returns ``(dq, dk, dv)``.
 
     ``o`` and ``lse`` must be what ``fwd`` returned for the same inputs, scale
     and causal flag.  ``workspace`` (a uint8 GPU tensor of at least
@@ -134,8 +137,11 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, w
     """
     lib = load()
     B, H, N, d = q.shape
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"unsupported dtype {dtype}")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, n, torch.bfloat16, (B, H, N, d))
+        _check(t, n, dtype, (B, H, N, d))
     _check(lse, "lse", torch.float32, (B, H, N))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -147,14 +153,15 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, w
     else:
         dq, dk, dv = out
         for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-            _check(t, n, torch.bfloat16, (B, H, N, d))
+            _check(t, n, dtype, (B, H, N, d))
     if workspace is not None:
         _check(workspace, "workspace", torch.uint8)
-    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
-                    workspace.data_ptr(), workspace.numel(), _stream())
+    name = "fa_bwd" if dtype == torch.bfloat16 else "fa_bwd_fp16"
+    st = getattr(lib, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                            workspace.data_ptr(), workspace.numel(), _stream())
     if st != 0:
-        raise FAError(st, "fa_bwd")
+        raise FAError(st, name)
     return dq, dk, dv
 
 

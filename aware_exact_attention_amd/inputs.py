@@ -8,7 +8,8 @@ float64) read exactly these values.
 Recipe: ``torch.Generator().manual_seed(seed)``, then ``torch.randn`` in
 float32 on the CPU for Q, K, V and, for backward workloads, dO, in that order.
 ``qk_std`` multiplies Q and K in float32 before the single round-to-nearest-even
-conversion to bfloat16 (float32 workloads are not rounded).
+conversion to bfloat16 (or float16 for ``dtype="fp16"``; float32 workloads are
+not rounded).
 
 The shapes follow the pages' workloads: the benchmark harness of the
 FlashAttention-2 principle and deployment page (B=1, H=8, d=128, bf16 randn,
@@ -30,7 +31,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str            # "bf16" or "f32"
+    dtype: str            # "bf16", "fp16" or "f32"
     causal: bool
     seed: int
     qk_std: float = 1.0
@@ -80,6 +81,8 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int =
             x = x * qk_std
         if dtype == "bf16":
             x = x.to(torch.bfloat16)
+        elif dtype == "fp16":
+            x = x.to(torch.float16)
         elif dtype != "f32":
             raise ValueError(f"unknown dtype {dtype!r}")
         out.append(x.contiguous())
@@ -91,5 +94,5 @@ def workload_inputs(w: Workload):
 
 
 def to_f64(t: torch.Tensor):
-    """Widen a CPU tensor to a float64 numpy array (exact for bf16 and fp32)."""
+    """Widen a CPU tensor to a float64 numpy array (exact for bf16, fp16 and fp32)."""
     return t.detach().to("cpu", torch.float64).numpy()

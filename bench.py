@@ -39,7 +39,7 @@ CSRC = os.path.join(ROOT, "aware_exact_attention_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_traffic_B1H8N16384d128.txt")
 COPY_BYTES = 1 << 30          # size of the calibration copy (read and written once each)
 # kernels of one step, as named in rocprofv3 output
-FWD_KERNELS = ("fwd_bf16_kernel",)
+FWD_KERNELS = ("fwd_kernel",)
 BWD_KERNELS = ("bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
 
 
@@ -181,8 +181,8 @@ def _graph_ms(fn, calls: int, warmup: int = 3) -> float:
 
 def next_rows():
     """Key-split forward (fa_fwd_splitkv) against fa_fwd on grids too small to fill
-    the GPU, the sliding-window and block-sparse forwards, and the Eq. (2) merge
-    kernel (fa_lse_merge) against the HBM roof."""
+    the GPU, the sliding-window and block-sparse forwards, fp16 inputs, and the
+    Eq. (2) merge kernel (fa_lse_merge) against the HBM roof."""
     res = {}
     for name, (B, H, N, d, causal) in {"B1H8N2048d128": (1, 8, 2048, 128, False),
                                        "B1H4N4096d128_causal": (1, 4, 4096, 128, True),
@@ -223,6 +223,20 @@ def next_rows():
         "ms": round(t_b, 5), "kept_blocks": round(kept / nb / nb, 4), "dense_fa_fwd_ms": round(t_d, 5),
         "tflops_visible": round(fl_b / (t_b * 1e-3) / 1e12, 1),
         "frac_peak": round(fl_b / (t_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    # fp16 inputs at the benchmark shape (fa_fwd_fp16, fa_bwd_fp16)
+    q16, k16, v16, do16 = (t.cuda() for t in make_inputs(B, H, N, d, "fp16", 9, 1.0, backward=True))
+    o16 = torch.empty_like(q16)
+    grads16 = tuple(torch.empty_like(q16) for _ in range(3))
+    ws16 = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    t_f16 = _graph_ms(lambda: fa.fwd(q16, k16, v16, out=o16, lse=lse), 3)
+    t_b16 = _graph_ms(lambda: fa.bwd(q16, k16, v16, o16, lse, do16, workspace=ws16, out=grads16), 3)
+    fl_f = 4 * B * H * N * N * d
+    res["fp16_B1H8N16384d128"] = {
+        "fwd_ms": round(t_f16, 5), "fwd_tflops": round(fl_f / (t_f16 * 1e-3) / 1e12, 1),
+        "fwd_frac_peak": round(fl_f / (t_f16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "bwd_ms": round(t_b16, 5), "bwd_tflops": round(2.5 * fl_f / (t_b16 * 1e-3) / 1e12, 1),
+        "bwd_frac_peak": round(2.5 * fl_f / (t_b16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "peak_note": "fp16 dense MFMA peak equals bf16's (2516.6 TFLOP/s)"}
     # merge kernel alone: S = 4 parts of B1 H8 N2048 d128
     S, B, H, N, d = 4, 1, 8, 2048, 128
     g = torch.Generator().manual_seed(9)
@@ -316,7 +330,7 @@ def main():
     r_bwd["kernel"] = ("fa_bwd: bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel (one HIP event pair around the "
                        "call); FLOP = 10*B*H*N^2*d algorithmic (the dQ pass's recompute of S and dP not counted)")
     r_fwd = roof(w.fwd_flop, f_ms, "fwd")
-    r_fwd["kernel"] = "fa_fwd: fwd_bf16_kernel; FLOP = 4*B*H*N^2*d"
+    r_fwd["kernel"] = "fa_fwd: fwd_kernel (bf16, 8 waves); FLOP = 4*B*H*N^2*d"
     bytes_fwd = w.B * w.H * w.N * (8 * w.d + 4)
     bytes_bwd = w.B * w.H * w.N * (16 * w.d + 12)
 

@@ -114,6 +114,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fa_fwd_fp16, fa_bwd_fp16 - fp16 (IEEE binary16) versions of fa_fwd and
+ * fa_bwd with identical parameter lists and conventions: every [B][H][N][d]
+ * tensor (q, k, v, o, dO, dq, dk, dv) is _Float16 instead of __bf16, the
+ * products run on the fp16 MFMA with fp32 accumulation, and the values
+ * rounded to 16 bits (P and dS for the second products, the outputs) are
+ * rounded to fp16 (round-to-nearest-even).  lse and the workspace are as in
+ * fa_fwd / fa_bwd (fa_bwd_workspace_bytes gives the size).  For the FP16 half
+ * of the pages' mixed precision (FlashAttention optimisation page, section
+ * 6.2: FP16/BF16 storage with the statistics kept in fp32).
+ */
+int fa_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+int fa_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * fa_fwd_splitkv_parts - number of key parts fa_fwd_splitkv uses for these
  * sizes and this num_splits (<= 0: automatic), or 0 if the sizes are
  * invalid.  The keys of every row are cut into ranges of whole 64-key tiles;

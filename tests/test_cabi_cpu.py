@@ -38,6 +38,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_bytes", "fa_bwd",
+                                           "fa_fwd_fp16", "fa_bwd_fp16",
                                            "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_bytes",
                                            "fa_fwd_splitkv", "fa_lse_merge", "fa_fwd_window",
                                            "fa_fwd_blocksparse", "fa_status_string"])
@@ -77,7 +78,7 @@ def _fwd_args(B=1, H=1, N=8, d=64):
     return bufs, [b.ptr for b in bufs]
 
 
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp16"])
 def test_fwd_validation(lib, fn):
     f = getattr(lib, fn)
     bufs, (q, k, v, o, l) = _fwd_args()
@@ -109,7 +110,8 @@ def test_bwd_workspace_bytes(lib):
     assert lib.fa_bwd_workspace_bytes(1, 1, 100, 80) == 0
 
 
-def test_bwd_validation(lib):
+@pytest.mark.parametrize("fn", ["fa_bwd", "fa_bwd_fp16"])
+def test_bwd_validation(lib, fn):
     B, H, N, d = 1, 2, 16, 64
     bufs = [_Buf(B * H * N * d * 2) for _ in range(9)]
     q, k, v, o, lse, do, dq, dk, dv = [b.ptr for b in bufs]
@@ -124,7 +126,7 @@ def test_bwd_validation(lib):
                  "wsb", "stream"]
         for kk, vv in ch.items():
             a[names.index(kk)] = vv
-        return lib.fa_bwd(*a)
+        return getattr(lib, fn)(*a)
 
     assert call(do=None) == ST["NULL"]
     assert call(dk=None) == ST["NULL"]
