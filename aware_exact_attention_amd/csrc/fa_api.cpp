@@ -17,6 +17,12 @@ hipError_t launch_fwd_fp16(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                            int causal, void* ws, hipStream_t st);
+hipError_t launch_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                              int N, int d, float scale, int causal, float p, unsigned long long seed,
+                              hipStream_t st);
+hipError_t launch_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                              int causal, float p, unsigned long long seed, void* ws, hipStream_t st);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                           int N, int d, float scale, int causal, hipStream_t st);
 hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -100,6 +106,35 @@ int fa_bwd_fp16(const void* q, const void* k, const void* v, const void* o, cons
   if (st != fa::kOk) return st;
   return fa::launch_bwd_fp16(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, workspace, stream) ==
                  hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, float dropout_p, unsigned long long seed, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_fwd(q, k, v, o, lse, s, scale, causal, 2);
+  if (st == fa::kOk) st = fa::check_dropout_p(dropout_p);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed, stream) == hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                   float dropout_p, unsigned long long seed, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, workspace, workspace_bytes);
+  if (st == fa::kOk) st = fa::check_dropout_p(dropout_p);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_bwd_dropout(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, dropout_p, seed,
+                                workspace, stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
 }

@@ -147,11 +147,11 @@ struct DkdvTile {
   static_assert(QT % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool DROP>
 __global__ void __launch_bounds__(512, 1)
 bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
                 const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
-                E* __restrict__ dK, E* __restrict__ dV, int N, int Tk, float c /* scale*log2(e) */,
+                E* __restrict__ dK, E* __restrict__ dV, DropArgs dp, int N, int Tk, float c /* scale*log2(e) */,
                 float scale) {
   using T = DkdvTile<D>;
   using v8 = typename Vec<E>::v8;
@@ -279,13 +279,24 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
         for (int g = 0; g < 4; ++g) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(sb + T::OFF_LSE + (qb * 32 + 8 * g + 4 * half) * 4);
           f32x4 p4;
+          // dropout: the keep bits of these 4 consecutive queries at this key;
+          // a dropped element is handed over with its sign bit set (P >= 0)
+          unsigned keep = 0xFu;
+          if constexpr (DROP) keep = keep_col4(dp, unsigned(qs + qb * 32 + 8 * g + 4 * half) >> 2, unsigned(key), unsigned(bh));
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float p = exp2_fast(fmaf(acc1[qb][4 * g + e], c, -l4[e]));
             if (need && key > qs + qb * 32 + 8 * g + 4 * half + e) p = 0.f;
-            p4[e] = p;
             const int j = 4 * g + e;
-            op[qb * 2 + (j >> 3)][j & 7] = (E)p;
+            if constexpr (DROP) {
+              // the kept P for dV; its 1/(1-p) scale is applied to dV at the end
+              const bool kept = (keep >> e) & 1u;
+              p4[e] = kept ? p : -p;
+              op[qb * 2 + (j >> 3)][j & 7] = (E)(kept ? p : 0.f);
+            } else {
+              p4[e] = p;
+              op[qb * 2 + (j >> 3)][j & 7] = (E)p;
+            }
           }
           *reinterpret_cast<f32x4*>(xp + (qb * 4 + g) * 64 * 16) = p4;
         }
@@ -302,7 +313,18 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * g + e;
-            op[qb * 2 + (j >> 3)][j & 7] = (E)(p4[e] * (acc1[qb][j] - d4[e]));
+            if constexpr (DROP) {
+              // dP = Z * (dO V^T): dropped elements (sign bit set) contribute -P*D only.
+              // The element goes through its own register first: the compiler
+              // otherwise tests the sign of element 0 for all four.
+              float pe = p4[e];
+              asm volatile("" : "+v"(pe));
+              const bool kept = !(__builtin_bit_cast(unsigned, pe) >> 31);
+              const float dpz = kept ? acc1[qb][j] * dp.keep_scale : 0.f;
+              op[qb * 2 + (j >> 3)][j & 7] = (E)(fabsf(pe) * (dpz - d4[e]));
+            } else {
+              op[qb * 2 + (j >> 3)][j & 7] = (E)(p4[e] * (acc1[qb][j] - d4[e]));
+            }
           }
         }
     }
@@ -332,7 +354,7 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
 
   // ---- epilogue: dV = (dV^T)^T (A), dK = scale * (dK^T)^T (B); lane holds
   // key `key`, keys past N are dropped by the buffer bounds
-  const float f = role_a ? 1.f : scale;
+  const float f = role_a ? (DROP ? dp.keep_scale : 1.f) : scale;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc((role_a ? dV : dK) + head, head_bytes);
 #pragma unroll
   for (int b = 0; b < T::DB; ++b)
@@ -365,11 +387,11 @@ struct DqTile {
   static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
 
-template <typename E, int D, bool CAUSAL, int NW>
+template <typename E, int D, bool CAUSAL, int NW, bool DROP>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
 bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
               const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
-              E* __restrict__ dQ, int N, int Tr, float c /* scale*log2(e) */, float scale) {
+              E* __restrict__ dQ, DropArgs dp, int N, int Tr, float c /* scale*log2(e) */, float scale) {
   using T = DqTile<D, NW>;
   using v8 = typename Vec<E>::v8;
   __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
@@ -500,13 +522,26 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
     const int key0 = j * T::BC;
     const bool need = CAUSAL && (key0 + T::BC - 1 > wq0);
     v8 db[T::PS];
+    // dropout: registers 4m .. 4m+3 of a key block hold 4 consecutive keys of
+    // this lane's query, one Philox block row; dP = Z * (dO V^T)
+    unsigned keep = 0;
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          keep |= keep_row4(dp, unsigned(qrow), unsigned(key0 + kb * 32 + acc_row(4 * m, lane)) >> 2, unsigned(bh))
+                  << (kb * 16 + 4 * m);
+    }
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pr = exp2_fast(fmaf(s[kb][r], c, -lq));
         if (need && key0 + kb * 32 + acc_row(r, lane) > qrow) pr = 0.f;
-        db[kb * 2 + (r >> 3)][r & 7] = (E)(pr * (p[kb][r] - dd));
+        float dpv = p[kb][r];
+        if constexpr (DROP) dpv = ((keep >> (kb * 16 + r)) & 1u) ? dpv * dp.keep_scale : 0.f;
+        db[kb * 2 + (r >> 3)][r & 7] = (E)(pr * (dpv - dd));
       }
     // ---- dQ^T += K_j^T dS^T (k = key, in the accumulator's order)
     v8 ka = tr_pair<E>(base, tof[0][0], tof[0][1]);
@@ -557,10 +592,10 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool DROP = false>
 static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
-                               void* ws, hipStream_t st) {
+                               void* ws, hipStream_t st, DropArgs dp = DropArgs{}) {
   const long long rows = (long long)B * H * N;
   const BwdWorkspace w = bwd_workspace_layout(Shape{B, H, N, D});
   char* base = reinterpret_cast<char*>(ws);
@@ -584,19 +619,19 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   const int Tr = dq8 ? (N + DqTile<D, 8>::BR - 1) / DqTile<D, 8>::BR : (N + DqTile<D, 4>::BR - 1) / DqTile<D, 4>::BR;
   const long long Gq = (long long)B * H * Tr;
   if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, DROP>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
-                     (const float*)lse2, (const float*)Dv, (E*)dk, (E*)dv, N, Tk, c, scale);
+                     (const float*)lse2, (const float*)Dv, (E*)dk, (E*)dv, dp, N, Tk, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dq8)
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 8>), dim3((unsigned)Gq), dim3(DqTile<D, 8>::NT), 0, st,
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 8, DROP>), dim3((unsigned)Gq), dim3(DqTile<D, 8>::NT), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
-                       (const float*)lse2, (const float*)Dv, (E*)dq, N, Tr, c, scale);
+                       (const float*)lse2, (const float*)Dv, (E*)dq, dp, N, Tr, c, scale);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 4>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT), 0, st,
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 4, DROP>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
-                       (const float*)lse2, (const float*)Dv, (E*)dq, N, Tr, c, scale);
+                       (const float*)lse2, (const float*)Dv, (E*)dq, dp, N, Tr, c, scale);
   return hipGetLastError();
 }
 
@@ -615,6 +650,17 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                       int causal, void* ws, hipStream_t st) {
   return launch_bwd_e<__bf16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, ws, st);
+}
+
+hipError_t launch_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                              int causal, float p, unsigned long long seed, void* ws, hipStream_t st) {
+  const DropArgs dp = make_drop_args(p, seed);
+  if (d == 128)
+    return causal ? launch_bwd_t<__bf16, 128, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
+                  : launch_bwd_t<__bf16, 128, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
+  return causal ? launch_bwd_t<__bf16, 64, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
+                : launch_bwd_t<__bf16, 64, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
 }
 
 hipError_t launch_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -128,6 +130,81 @@ __device__ __forceinline__ unsigned pack2(float lo, float hi) {
   unsigned short ua = __builtin_bit_cast(unsigned short, a);
   unsigned short ub = __builtin_bit_cast(unsigned short, b);
   return unsigned(ua) | (unsigned(ub) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Dropout bits.  Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): ten rounds on a 128-bit counter and
+// a 64-bit key; a round forms the 64-bit products c0*0xD2511F53 and
+// c2*0xCD9E8D57 and returns (hi(c2*M1)^c1^k0, lo(c2*M1), hi(c0*M0)^c3^k1,
+// lo(c0*M0)); the key is bumped by 0x9E3779B9 and 0xBB67AE85 between rounds.
+//
+// Element (b, h, i, j) of P belongs to the 4 x 4 block (i/4, j/4), whose call
+// has counter (i/4, j/4, b*H+h, 0) and key (seed lo, seed hi); word i%4, byte
+// j%4 (little-endian) is the element's 8-bit draw, and the element is kept
+// iff the draw is >= t.  Kept probabilities are scaled by keep_scale.
+// ---------------------------------------------------------------------------
+struct DropArgs {
+  unsigned t;        // 8-bit threshold, 0..255 (0: keep everything)
+  float keep_scale;  // 1 / (1 - t/256)
+  unsigned k0, k1;   // the seed
+};
+
+// Host side: threshold t = round(256 p) clamped to [0, 255], so the
+// effective drop probability is t / 256, and keep_scale = 1 / (1 - t/256).
+inline DropArgs make_drop_args(float p, unsigned long long seed) {
+  double t = std::floor(256.0 * double(p) + 0.5);
+  if (t < 0.0) t = 0.0;
+  if (t > 255.0) t = 255.0;
+  DropArgs d;
+  d.t = unsigned(t);
+  d.keep_scale = float(1.0 / (1.0 - t / 256.0));
+  d.k0 = unsigned(seed & 0xFFFFFFFFull);
+  d.k1 = unsigned(seed >> 32);
+  return d;
+}
+
+__device__ __forceinline__ u32x4 philox4x32_10(unsigned c0, unsigned c1, unsigned c2, unsigned c3, unsigned k0,
+                                               unsigned k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const unsigned long long p0 = (unsigned long long)c0 * 0xD2511F53u;
+    const unsigned long long p1 = (unsigned long long)c2 * 0xCD9E8D57u;
+    const unsigned n0 = unsigned(p1 >> 32) ^ c1 ^ k0;
+    const unsigned n2 = unsigned(p0 >> 32) ^ c3 ^ k1;
+    c1 = unsigned(p1);
+    c3 = unsigned(p0);
+    c0 = n0;
+    c2 = n2;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// Keep bits (bit e = element e) of the 4 elements of one row and 4 consecutive
+// columns of a 4 x 4 block: query `i`, keys 4*j4 .. 4*j4+3.
+__device__ __forceinline__ unsigned keep_row4(const DropArgs& dp, unsigned i, unsigned j4, unsigned bh) {
+  const u32x4 w = philox4x32_10(i >> 2, j4, bh, 0u, dp.k0, dp.k1);
+  const unsigned s = i & 3u;
+  const unsigned word = s == 0 ? w[0] : s == 1 ? w[1] : s == 2 ? w[2] : w[3];
+  unsigned bits = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bits |= unsigned(((word >> (8 * e)) & 0xFFu) >= dp.t) << e;
+  return bits;
+}
+
+// Keep bits of the 4 elements of one column and 4 consecutive rows of a block:
+// queries 4*i4 .. 4*i4+3 (bit e = query 4*i4+e), key `j`.
+__device__ __forceinline__ unsigned keep_col4(const DropArgs& dp, unsigned i4, unsigned j, unsigned bh) {
+  const u32x4 w = philox4x32_10(i4, j >> 2, bh, 0u, dp.k0, dp.k1);
+  const unsigned sh = 8 * (j & 3u);
+  unsigned bits = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bits |= unsigned(((w[e] >> sh) & 0xFFu) >= dp.t) << e;
+  return bits;
 }
 
 // Map a linear workgroup id to a tile id so that the tiles of one (b, h)

@@ -80,15 +80,16 @@ struct MaskArgs {
   int nb, H;
 };
 
-template <typename E, int D, bool CAUSAL, int NW, bool SPLIT, int MODE>
+template <typename E, int D, bool CAUSAL, int NW, bool SPLIT, int MODE, bool DROP>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
 fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V, E* __restrict__ O,
-           float* __restrict__ LSE, int N, int Tr, float c, SplitArgs sp, MaskArgs mk) {
+           float* __restrict__ LSE, int N, int Tr, float c, SplitArgs sp, MaskArgs mk, DropArgs dp) {
   using T = FwdTile<D, NW>;
   using v8 = typename Vec<E>::v8;
   using v4 = typename Vec<E>::v4;
   constexpr bool WINDOW = MODE == kMaskWindow, BLOCKS = MODE == kMaskBlocks;
   static_assert(!(SPLIT && MODE != kMaskDense), "key split only with the dense or causal mask");
+  static_assert(!DROP || (!SPLIT && MODE == kMaskDense), "dropout only on the plain forward");
   static_assert(!BLOCKS || (T::BC == kMaskBlock && T::BR == 2 * kMaskBlock), "mask blocks are key tiles and half a row block");
   __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
   __shared__ unsigned short tlist[BLOCKS ? kMaxMaskTiles : 1];
@@ -298,7 +299,21 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
 #pragma unroll
       for (int b = 0; b < T::DB; ++b) o[b] *= alpha;
     }
-    // P, rounded to bf16 for the PV product; l sums the fp32 values
+    // P, rounded to the input type for the PV product; l sums the fp32 values
+    // (before dropout: the statistic is that of the softmax itself).  With
+    // dropout, bit kb*16 + r of `keep` says whether element (kb, r) survives:
+    // registers 4m .. 4m+3 of a key block hold 4 consecutive keys of this row,
+    // one Philox block row.
+    unsigned keep = 0;
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const unsigned key = unsigned(j * T::BC + kb * 32 + acc_row(4 * m, lane));
+          keep |= keep_row4(dp, unsigned(qrow), key >> 2, unsigned(bh)) << (kb * 16 + 4 * m);
+        }
+    }
     v8 pb[T::PS];
     float rs = 0.f;
 #pragma unroll
@@ -307,7 +322,9 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_fast(fmaf(s[kb][r], c, -mu));
         rs += p;
-        pb[kb * 2 + (r >> 3)][r & 7] = (E)p;
+        float pd = p;  // dropout: the kept P; the 1/(1-p) scale is applied to O at the end
+        if constexpr (DROP) pd = ((keep >> (kb * 16 + r)) & 1u) ? p : 0.f;
+        pb[kb * 2 + (r >> 3)][r & 7] = (E)pd;
       }
     l += rs;
     // ---- O^T += V_j^T P^T: DB independent chains; V^T operands come from two
@@ -373,8 +390,10 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
       sp.LP[size_t(part) * sp.part_rows + size_t(bh) * N + qrow] = lt > 0.f ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
     return;
   }
-  // a row that saw no key (block-sparse masks only): O = 0, LSE = -inf
-  const float inv = (!BLOCKS || lt > 0.f) ? 1.f / lt : 0.f;
+  // a row that saw no key (block-sparse masks only): O = 0, LSE = -inf;
+  // dropout scales the kept terms by 1/(1-p) here, in fp32
+  float inv = (!BLOCKS || lt > 0.f) ? 1.f / lt : 0.f;
+  if constexpr (DROP) inv *= dp.keep_scale;
   // rows past N are dropped by the buffer bounds
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head, head_bytes);
 #pragma unroll
@@ -487,16 +506,16 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, int NW>
+template <typename E, int D, bool CAUSAL, int NW, bool DROP = false>
 static hipError_t launch_fwd_nw(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                                int N, float scale, hipStream_t st) {
+                                int N, float scale, hipStream_t st, DropArgs dp = DropArgs{}) {
   using T = FwdTile<D, NW>;
   const int Tr = (N + T::BR - 1) / T::BR;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, NW, false, kMaskDense>), dim3((unsigned)G), dim3(T::NT), 0, st,
-                     (const E*)q, (const E*)k, (const E*)v, (E*)o, lse, N, Tr, scale * kLog2e,
-                     SplitArgs{1, 0, nullptr, nullptr, 0, 0}, MaskArgs{});
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, NW, false, kMaskDense, DROP>), dim3((unsigned)G), dim3(T::NT), 0,
+                     st, (const E*)q, (const E*)k, (const E*)v, (E*)o, lse, N, Tr, scale * kLog2e,
+                     SplitArgs{1, 0, nullptr, nullptr, 0, 0}, MaskArgs{}, dp);
   return hipGetLastError();
 }
 
@@ -531,6 +550,27 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, int causal, hipStream_t st) {
   return launch_fwd_e<_Float16>(q, k, v, o, lse, B, H, N, d, scale, causal, st);
+}
+
+// Forward with dropout on P (bf16): the plain forward's tiles and launch
+// shape, with the keep bits of each tile drawn in the kernel.
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_dropout_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                       int H, int N, float scale, const DropArgs& dp, hipStream_t st) {
+  const long long G8 = (long long)B * H * ((N + FwdTile<D, 8>::BR - 1) / FwdTile<D, 8>::BR);
+  if (D == 128 && !CAUSAL && G8 >= kNumCUs)
+    return launch_fwd_nw<__bf16, D, CAUSAL, 8, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
+  return launch_fwd_nw<__bf16, D, CAUSAL, 4, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
+}
+
+hipError_t launch_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                              int N, int d, float scale, int causal, float p, unsigned long long seed,
+                              hipStream_t st) {
+  const DropArgs dp = make_drop_args(p, seed);
+  if (d == 128) return causal ? launch_fwd_dropout_t<128, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
+                              : launch_fwd_dropout_t<128, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
+  return causal ? launch_fwd_dropout_t<64, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
+                : launch_fwd_dropout_t<64, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -626,9 +666,9 @@ static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v
   char* base = reinterpret_cast<char*>(ws);
   SplitArgs sp{S, (Tc + S - 1) / S, reinterpret_cast<float*>(base + w.o_parts),
                reinterpret_cast<float*>(base + w.lse_parts), (long long)B * H * N * D, (long long)B * H * N};
-  hipLaunchKernelGGL((fwd_kernel<__bf16, D, CAUSAL, 4, true, kMaskDense>), dim3((unsigned)G), dim3(T::NT), 0, st,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
-                     scale * kLog2e, sp, MaskArgs{});
+  hipLaunchKernelGGL((fwd_kernel<__bf16, D, CAUSAL, 4, true, kMaskDense, false>), dim3((unsigned)G), dim3(T::NT), 0,
+                     st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
+                     scale * kLog2e, sp, MaskArgs{}, DropArgs{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_lse_merge(sp.OP, sp.LP, S, o, lse, B, H, N, D, st);
@@ -651,9 +691,9 @@ static hipError_t launch_fwd_masked_t(const void* q, const void* k, const void* 
   const int Tr = (N + T::BR - 1) / T::BR;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<__bf16, D, CAUSAL, 4, false, MODE>), dim3((unsigned)G), dim3(T::NT), 0, st,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
-                     scale * kLog2e, SplitArgs{1, 0, nullptr, nullptr, 0, 0}, mk);
+  hipLaunchKernelGGL((fwd_kernel<__bf16, D, CAUSAL, 4, false, MODE, false>), dim3((unsigned)G), dim3(T::NT), 0,
+                     st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
+                     scale * kLog2e, SplitArgs{1, 0, nullptr, nullptr, 0, 0}, mk, DropArgs{});
   return hipGetLastError();
 }
 

@@ -245,6 +245,9 @@ inline int validate_fwd_blocksparse(const void* q, const void* k, const void* v,
   return kOk;
 }
 
+// Dropout probability: finite, 0 <= p < 1.
+inline int check_dropout_p(float p) { return (std::isfinite(p) && p >= 0.0f && p < 1.0f) ? kOk : kErrArg; }
+
 inline const char* status_string(int st) {
   switch (st) {
     case kOk: return "FA_OK: success";
@@ -256,7 +259,7 @@ inline const char* status_string(int st) {
     case kErrWorkspace: return "FA_ERR_WORKSPACE: workspace missing or smaller than the *_workspace_bytes() size";
     case kErrDevice: return "FA_ERR_DEVICE: the current device is not a gfx950 GPU";
     case kErrHip: return "FA_ERR_HIP: a HIP launch or runtime call failed";
-    case kErrArg: return "FA_ERR_ARG: causal must be 0 or 1, a part count in range, and outputs must not alias inputs";
+    case kErrArg: return "FA_ERR_ARG: causal must be 0 or 1, counts and probabilities in range, and outputs must not alias inputs";
     default: return "unknown fa_status";
   }
 }

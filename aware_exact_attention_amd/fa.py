@@ -39,6 +39,10 @@ SIGNATURES = {
                                _vp]),
     "fa_fwd_blocksparse": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp,
                                     _c_int, _vp]),
+    "fa_fwd_dropout": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_float,
+                                ctypes.c_ulonglong, _vp]),
+    "fa_bwd_dropout": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                _c_int, _c_float, ctypes.c_ulonglong, _vp, _c_size_t, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -293,3 +297,51 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
     if st != 0:
         raise FAError(st, "fa_fwd_blocksparse")
     return out, lse
+
+
+def fwd_dropout(q, k, v, dropout_p: float, seed: int, causal: bool = False, scale: float | None = None,
+                out=None, lse=None):
+    """bf16 forward with dropout on P (Philox4x32-10 mask from ``seed``); returns ``(o, lse)``."""
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,N,d]")
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _fwd_outputs(q, out, lse)
+    st = lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                            float(scale), int(bool(causal)), float(dropout_p), int(seed) & (2**64 - 1), _stream())
+    if st != 0:
+        raise FAError(st, "fa_fwd_dropout")
+    return out, lse
+
+
+def bwd_dropout(q, k, v, o, lse, do, dropout_p: float, seed: int, causal: bool = False,
+                scale: float | None = None, workspace=None, out=None):
+    """bf16 backward through the same dropout mask as ``fwd_dropout``; returns ``(dq, dk, dv)``."""
+    lib = load()
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    _check(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", torch.uint8)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            _check(t, n, torch.bfloat16, (B, H, N, d))
+    st = lib.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                            float(dropout_p), int(seed) & (2**64 - 1), workspace.data_ptr(), workspace.numel(),
+                            _stream())
+    if st != 0:
+        raise FAError(st, "fa_bwd_dropout")
+    return dq, dk, dv

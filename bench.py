@@ -181,8 +181,8 @@ def _graph_ms(fn, calls: int, warmup: int = 3) -> float:
 
 def next_rows():
     """Key-split forward (fa_fwd_splitkv) against fa_fwd on grids too small to fill
-    the GPU, the sliding-window and block-sparse forwards, fp16 inputs, and the
-    Eq. (2) merge kernel (fa_lse_merge) against the HBM roof."""
+    the GPU, the sliding-window and block-sparse forwards, fp16 inputs, dropout,
+    and the Eq. (2) merge kernel (fa_lse_merge) against the HBM roof."""
     res = {}
     for name, (B, H, N, d, causal) in {"B1H8N2048d128": (1, 8, 2048, 128, False),
                                        "B1H4N4096d128_causal": (1, 4, 4096, 128, True),
@@ -237,6 +237,15 @@ def next_rows():
         "bwd_ms": round(t_b16, 5), "bwd_tflops": round(2.5 * fl_f / (t_b16 * 1e-3) / 1e12, 1),
         "bwd_frac_peak": round(2.5 * fl_f / (t_b16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "peak_note": "fp16 dense MFMA peak equals bf16's (2516.6 TFLOP/s)"}
+    # dropout p = 0.1 at the benchmark shape (fa_fwd_dropout, fa_bwd_dropout)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    dob = torch.randn(q.shape, generator=torch.Generator().manual_seed(10)).to(torch.bfloat16).cuda()
+    t_fd = _graph_ms(lambda: fa.fwd_dropout(q, k, v, 0.1, 1234, out=o, lse=lse), 3)
+    t_bd = _graph_ms(lambda: fa.bwd_dropout(q, k, v, o, lse, dob, 0.1, 1234, workspace=ws16, out=grads), 3)
+    res["dropout_p0.1_B1H8N16384d128"] = {
+        "fwd_ms": round(t_fd, 5), "fwd_tflops": round(fl_f / (t_fd * 1e-3) / 1e12, 1),
+        "bwd_ms": round(t_bd, 5), "bwd_tflops": round(2.5 * fl_f / (t_bd * 1e-3) / 1e12, 1),
+        "note": "FLOP of the attention products only; the mask's Philox draws are VALU work on top"}
     # merge kernel alone: S = 4 parts of B1 H8 N2048 d128
     S, B, H, N, d = 4, 1, 8, 2048, 128
     g = torch.Generator().manual_seed(9)

@@ -132,6 +132,32 @@ int fa_bwd_fp16(const void* q, const void* k, const void* v, const void* o, cons
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fa_fwd_dropout, fa_bwd_dropout - bf16 forward and backward with dropout on
+ * the attention probabilities (the Journal of Software 2026(1) p.218 survey
+ * lists dropout among the operations fused into the kernel, sentence after
+ * Eq. (2)).  Parameters as fa_fwd / fa_bwd plus:
+ *   dropout_p: drop probability, 0 <= p < 1 (else FA_ERR_ARG); it is applied as
+ *     t = round(256 p) clamped to 255 (effective probability t/256), and kept
+ *     probabilities are scaled by 1 / (1 - t/256);
+ *   seed: 64-bit key of the Philox4x32-10 counter-based generator (Salmon et
+ *     al., SC 2011).  Element (b, h, i, j) takes byte j%4 of word i%4 of the
+ *     call with counter (i/4, j/4, b*H+h, 0) and key (seed lo, seed hi) and is
+ *     kept iff that byte is >= t.  The mask is regenerated, not stored: the
+ *     backward must receive the same p, seed, scale and causal as the forward.
+ * Forward: o = (P * Z) V with Z = keep / (1 - t/256); lse is the statistic of
+ * the softmax before dropout.  Backward: gradients of sum(o * dO) through the
+ * same mask; fa_bwd_workspace_bytes gives the workspace size.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float dropout_p, unsigned long long seed, hipStream_t stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float dropout_p, unsigned long long seed,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * fa_fwd_splitkv_parts - number of key parts fa_fwd_splitkv uses for these
  * sizes and this num_splits (<= 0: automatic), or 0 if the sizes are
  * invalid.  The keys of every row are cut into ranges of whole 64-key tiles;

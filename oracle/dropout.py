@@ -64,19 +64,28 @@ def threshold(p: float) -> int:
     return int(min(255, max(0, int(np.floor(256.0 * p + 0.5)))))
 
 
-def keep_mask(B: int, H: int, N: int, seed: int, p: float) -> np.ndarray:
-    """``[B,H,N,N]`` bool: element (b, h, i, j) kept under the scheme in the module notes."""
+def keep_mask_bh(N: int, bh: int, seed: int, p: float) -> np.ndarray:
+    """``[N, N]`` bool keep mask of the head whose counter word is ``bh`` (= b*H + h)."""
     t = threshold(p)
     i = np.broadcast_to(np.arange(N)[:, None], (N, N))  # query index
     j = np.broadcast_to(np.arange(N)[None, :], (N, N))  # key index
+    words = np.stack(philox4x32(i // 4, j // 4, np.full((N, N), bh), np.zeros((N, N)),
+                                seed & MASK32, seed >> 32))            # [4, N, N]
+    w = np.take_along_axis(words, (i % 4)[None], axis=0)[0]           # word i % 4
+    u = (w >> (8 * (j % 4)).astype(np.uint64)) & np.uint64(0xFF)      # byte j % 4
+    return u >= t
+
+
+def keep_mask(B: int, H: int, N: int, seed: int, p: float, bh0: int = 0) -> np.ndarray:
+    """``[B,H,N,N]`` bool: element (b, h, i, j) kept, with head counter ``bh0 + b*H + h``.
+
+    ``bh0`` lets a caller evaluate a slice of heads of a larger tensor (for
+    B = 1, head h of an H-head tensor is ``keep_mask(1, 1, N, seed, p, bh0=h)``).
+    """
     out = np.empty((B, H, N, N), dtype=bool)
     for b in range(B):
         for h in range(H):
-            words = np.stack(philox4x32(i // 4, j // 4, np.full((N, N), b * H + h), np.zeros((N, N)),
-                                        seed & MASK32, seed >> 32))            # [4, N, N]
-            w = np.take_along_axis(words, (i % 4)[None], axis=0)[0]           # word i % 4
-            u = (w >> (8 * (j % 4)).astype(np.uint64)) & np.uint64(0xFF)      # byte j % 4
-            out[b, h] = u >= t
+            out[b, h] = keep_mask_bh(N, bh0 + b * H + h, seed, p)
     return out
 
 
@@ -84,11 +93,11 @@ def dropout_scale(p: float) -> float:
     return 1.0 / (1.0 - threshold(p) / 256.0)
 
 
-def ref_fwd_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int):
-    """``(O, LSE)`` with dropout on P; LSE is the pre-dropout statistic."""
+def ref_fwd_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, bh0: int = 0):
+    """``(O, LSE)`` with dropout on P; LSE is the pre-dropout statistic (``bh0`` as in keep_mask)."""
     q, k, v = _as_f64(q, k, v)
     B, H, N, _ = q.shape
-    z = keep_mask(B, H, N, seed, p) * dropout_scale(p)
+    z = keep_mask(B, H, N, seed, p, bh0) * dropout_scale(p)
     o = np.empty((B, H, N, v.shape[-1]))
     lse = np.empty((B, H, N))
     for b in range(B):
@@ -99,11 +108,11 @@ def ref_fwd_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int):
     return o, lse
 
 
-def ref_bwd_dropout(q, k, v, do, scale: float, causal: bool, p: float, seed: int):
+def ref_bwd_dropout(q, k, v, do, scale: float, causal: bool, p: float, seed: int, bh0: int = 0):
     """Gradients ``(dQ, dK, dV)`` of ``sum(O * dO)`` for the dropout forward above."""
     q, k, v, do = _as_f64(q, k, v, do)
     B, H, N, _ = q.shape
-    z = keep_mask(B, H, N, seed, p) * dropout_scale(p)
+    z = keep_mask(B, H, N, seed, p, bh0) * dropout_scale(p)
     dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     for b in range(B):
         for h in range(H):

@@ -38,7 +38,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_bytes", "fa_bwd",
-                                           "fa_fwd_fp16", "fa_bwd_fp16",
+                                           "fa_fwd_fp16", "fa_bwd_fp16", "fa_fwd_dropout", "fa_bwd_dropout",
                                            "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_bytes",
                                            "fa_fwd_splitkv", "fa_lse_merge", "fa_fwd_window",
                                            "fa_fwd_blocksparse", "fa_status_string"])
@@ -219,6 +219,24 @@ def test_mask_validation(lib):
     assert fb(q, k, v, o, l, B, H, N, d, 0.125, 0, o, 1, None) == ST["ARG"]      # mask overlaps the output
 
 
+def test_dropout_validation(lib):
+    bufs, (q, k, v, o, l) = _fwd_args()
+    f = lib.fa_fwd_dropout
+    assert f(None, k, v, o, l, 1, 1, 8, 64, 0.125, 0, 0.1, 7, None) == ST["NULL"]
+    assert f(q, k, v, o, l, 1, 1, 8, 64, 0.125, 0, -0.1, 7, None) == ST["ARG"]
+    assert f(q, k, v, o, l, 1, 1, 8, 64, 0.125, 0, 1.0, 7, None) == ST["ARG"]
+    assert f(q, k, v, o, l, 1, 1, 8, 64, 0.125, 0, float("nan"), 7, None) == ST["ARG"]
+    assert f(q, k, v, o, l, 1, 1, 8, 96, 0.125, 0, 0.1, 7, None) == ST["HEAD_DIM"]
+    B, H, N, d = 1, 2, 16, 64
+    bb = [_Buf(B * H * N * d * 2) for _ in range(9)]
+    ptrs = [b.ptr for b in bb]
+    need = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    ws = _Buf(need)
+    g = lib.fa_bwd_dropout
+    assert g(*ptrs, B, H, N, d, 0.125, 0, 1.5, 7, ws.ptr, need, None) == ST["ARG"]
+    assert g(*ptrs, B, H, N, d, 0.125, 0, 0.2, 7, None, 0, None) == ST["WORKSPACE"]
+
+
 def test_validate_header_with_gxx(tmp_path):
     """Host unit test of fa_validate.h compiled by g++ (no HIP, no GPU)."""
     src = tmp_path / "t.cpp"
@@ -278,6 +296,8 @@ int main() {
   EXPECT(validate_fwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 1, nullptr, 1) == kErrNull);
   EXPECT(validate_fwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 1, mem[3], 1) == kErrArg);
   EXPECT(validate_fwd_window(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f) == kOk);
+  EXPECT(check_dropout_p(0.0f) == kOk && check_dropout_p(0.999f) == kOk);
+  EXPECT(check_dropout_p(1.0f) == kErrArg && check_dropout_p(-1e-9f) == kErrArg && check_dropout_p(NAN) == kErrArg);
   return fails ? 1 : 0;
 }
 ''')

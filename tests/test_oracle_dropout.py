@@ -85,6 +85,8 @@ def pin_keep_rate(R):
         assert abs(m.mean() - keep) < 5 * sd, (p, m.mean(), keep)
         # a different seed or head gives a different mask
         assert (m[0, 0] != m[0, 1]).mean() > 0.1
+        # a slice of heads evaluated on its own sees the same mask
+        assert np.array_equal(R.keep_mask(1, 1, 512, 2024, p, bh0=1)[0, 0], m[0, 1])
     assert R.threshold(0.0) == 0 and R.threshold(0.5) == 128 and R.threshold(0.999) == 255
     assert abs(R.dropout_scale(0.5) - 2.0) < 1e-15
 
