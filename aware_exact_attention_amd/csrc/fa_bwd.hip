@@ -12,16 +12,18 @@
 //
 // Three kernels on the caller's stream, none of them with atomics:
 //  1. bwd_pre: D = rowsum(dO * O) and LSE in base-2 units, both fp32.
-//  2. bwd_dkdv: one workgroup per (b, h, 128-key block), eight waves in four
-//     pairs of 32 keys.  K (or V) of those keys stays in VGPRs as the B
-//     operand of S = Q K^T (or dP = dO V^T), so each lane holds one key and
-//     the recomputed P (or dS) feeds dV^T += dO^T P (or dK^T += Q^T dS)
+//  2. bwd_dkdv: one workgroup per (b, h, 128-key block), four waves of 32
+//     keys, one wave per SIMD.  K and V of a wave's keys stay in registers as
+//     the B operands of S = Q K^T and dP = dO V^T, so each lane holds one key
+//     and the recomputed P and dS feed dV^T += dO^T P and dK^T += Q^T dS
 //     straight from registers; dK^T and dV^T accumulate on chip for the whole
 //     sweep.  The workgroup streams 64-query steps (causal: from the diagonal
 //     on).  Q, dO and the per-row LSE and D of step i+1 go from HBM straight
 //     into LDS (buffer loads with the LDS destination) while step i computes;
 //     Q and dO are stored row-major only, and the transposed operands Q^T and
-//     dO^T are read with ds_read_b64_tr_b16.
+//     dO^T are read with ds_read_b64_tr_b16.  Within a step the wave issues
+//     its MFMAs in a fixed order and spreads the exponentials and the dS
+//     arithmetic over the MFMAs that do not depend on them.
 //  3. bwd_dq: one workgroup per (b, h, 128-query block), laid out like the
 //     forward kernel: each wave owns 32 queries whose Q and dO fragments stay
 //     in VGPRs, K and V tiles of 64 keys stream through double-buffered LDS,
@@ -35,6 +37,8 @@
 // rate that caps the whole backward well below the MFMA rate.
 #include "fa_common.h"
 #include "fa_validate.h"
+
+#include <utility>
 
 namespace fa {
 
@@ -113,22 +117,25 @@ bwd_pre_kernel(const E* __restrict__ O, const E* __restrict__ dO, const float* _
 // ---------------------------------------------------------------------------
 // 2. dK, dV: key-block-major sweep over the queries.
 //
-// Eight waves per workgroup, two per SIMD, in pairs that share 32 keys:
-//  * wave A (waves 0-3) holds K of its keys, forms S = Q K^T and
-//    P = exp2(S*c - LSE2), hands P to its partner through LDS and
-//    accumulates dV^T += dO^T P;
-//  * wave B (waves 4-7) holds V of the same keys, forms dP = dO V^T, reads P
-//    back and forms dS = P * (dP - D), and accumulates dK^T += Q^T dS.
-// Both roles run the same two products on different operands (Q and K vs dO
-// and V, then dO^T vs Q^T), so one wave's MFMAs overlap the other's VALU work
-// on the same SIMD, and each wave needs only one K/V fragment set and one
-// accumulator set.
+// Four waves per workgroup, one per SIMD, each owning 32 keys: K and V of
+// those keys stay in registers (parked in AGPRs, which the MFMAs read
+// directly) as the B operands of S = Q K^T and dP = dO V^T, so each lane
+// holds one key.  A wave runs all four products of a 64-query step itself:
+//   S = Q K^T, dP = dO V^T          (A operands: rows of the Q / dO tiles)
+//   P = exp2(S*c - LSE2), dS = P * (dP - D)   (VALU, one query per element)
+//   dV^T += dO^T P, dK^T += Q^T dS  (A operands: transposing reads of the
+//                                    same tiles; P and dS from registers)
+// The 64 MFMAs of a step (d = 128) are issued in a fixed order of slots,
+// and the VALU work is spread over the slots whose MFMAs do not depend on
+// it, two elements per slot: P of the first 32-query block while its dP
+// MFMAs run, its dS during the S MFMAs of the second block, and so on.
+// Each slot also issues the LDS read of the operand three slots ahead.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvTile {
-  static constexpr int NW = 8;
+  static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
-  static constexpr int BKV = 128;              // keys per workgroup, 32 per wave pair
+  static constexpr int BKV = 32 * NW;          // keys per workgroup, 32 per wave
   static constexpr int BQ = 64;                // queries per step
   static constexpr int QB = BQ / 32;           // 32-query blocks per step
   static constexpr int KS = D / 16;            // 16-wide k steps over d
@@ -140,28 +147,44 @@ struct DkdvTile {
   static constexpr int OFF_LSE = 2 * QT;       // BQ floats of LSE*log2(e)
   static constexpr int OFF_DD = 2 * QT + BQ * 4;  // BQ floats of D
   static constexpr int STAGE = 2 * QT + 2 * BQ * 4;
-  static constexpr int XP = 4 * QB * 4 * 64 * 16;  // P hand-over: 4 pairs x (QB*4 chunks of 16 B) x 64 lanes
-  static constexpr int OFF_XP = 2 * STAGE;
-  static constexpr int LDS = OFF_XP + XP;
+  static constexpr int LDS = 2 * STAGE;        // double-buffered
   static constexpr int LPW = QT / 1024 / NW;   // 1 KiB direct loads per wave per Q (or dO) tile
   static_assert(QT % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
+  // MFMA slots of one step: S, dP over block 0 and block 1 (2*M), then
+  // dV, dK over block 0's and block 1's queries (2*M); H per product and block
+  static constexpr int M = D / 8;
+  static constexpr int H = M / 2;
+  static constexpr int PF = 3;                 // operand reads in flight
+  static constexpr int PP = 8 / H;             // element pairs of VALU work per slot
+  // first slots of: P of block 0, dS of block 0, P of block 1, dS of block 1
+  static constexpr int P0 = H + 2, D0 = 2 * H + 1, P1 = 3 * H + 2, D1 = 4 * H + 1;
 };
 
+// Calls f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{})
+// in order, so that every index inside f is a compile-time constant.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 template <typename E, int D, bool CAUSAL, bool DROP>
-__global__ void __launch_bounds__(512, 1)
+__global__ void __launch_bounds__(256, 1)
 bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
                 const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
                 E* __restrict__ dK, E* __restrict__ dV, DropArgs dp, int N, int Tk, float c /* scale*log2(e) */,
                 float scale) {
   using T = DkdvTile<D>;
   using v8 = typename Vec<E>::v8;
+  constexpr int M = T::M, H = T::H, PF = T::PF;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const bool role_a = wave < 4;  // wave-uniform
-  const int pair = wave & 3;
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -171,17 +194,26 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
   const size_t head = size_t(bh) * N * D;
   const int head_bytes = N * T::RS;
 
-  // Fragments of this pair's keys: K (wave A) or V (wave B), the B operand of
-  // S = Q K^T or dP = dO V^T (lane: key kw0 + l32, d = 16*st + 8*half .. +7).
-  // Keys past N read as zero; their dK and dV rows are never stored.
-  const int kw0 = k0 + pair * 32;
-  const int key = kw0 + l32;
-  v8 kv[T::KS];
+  // K and V fragments of this wave's keys (lane: key k0 + 32*wave + l32,
+  // d = 16*st + 8*half .. +7).  Keys past N read as zero; their dK and dV
+  // rows are never stored.
+  const int key = k0 + wave * 32 + l32;
+  v8 kf[T::KS], vf[T::KS];
   {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc((role_a ? K : V) + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head, head_bytes);
 #pragma unroll
-    for (int st = 0; st < T::KS; ++st)
-      kv[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(r, key * T::RS + (16 * st + 8 * half) * 2, 0, 0));
+    for (int st = 0; st < T::KS; ++st) {
+      kf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rk, key * T::RS + (16 * st + 8 * half) * 2, 0, 0));
+      vf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rv, key * T::RS + (16 * st + 8 * half) * 2, 0, 0));
+    }
+    // Kept in AGPRs for the whole sweep: the MFMAs take them from there, and
+    // the VGPRs are left to the accumulators and the per-step values.
+#pragma unroll
+    for (int st = 0; st < T::KS; ++st) {
+      asm volatile("" : "+a"(kf[st]));
+      asm volatile("" : "+a"(vf[st]));
+    }
   }
 
   // Direct-to-LDS loads of the Q and dO tiles of a step: load u of this wave
@@ -207,26 +239,21 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
     if (wave == 1) load_lds4(make_rsrc(dh + q0, (N - q0) * 4), smem + stage * T::STAGE + T::OFF_DD, 4 * lane);
   };
 
-  // Operand tiles of the two products: rows of Q (A) or dO (B) for the first,
-  // transposed dO (A) or Q (B) for the second.
-  const int off_rows = role_a ? 0 : T::OFF_DO;
-  const int off_tr = role_a ? T::OFF_DO : 0;
+  // Operand offsets: rows l32 (+32 per block) of Q or dO, 16-byte unit
+  // 2*st + half; transposing reads as in tr_off.
   int rof[T::KS];
 #pragma unroll
-  for (int st = 0; st < T::KS; ++st) rof[st] = off_rows + l32 * T::RS + (((2 * st + half) ^ tile_swz<D>(l32)) * 16);
+  for (int st = 0; st < T::KS; ++st) rof[st] = l32 * T::RS + (((2 * st + half) ^ tile_swz<D>(l32)) * 16);
   int tof[T::DB][2];
 #pragma unroll
   for (int b = 0; b < T::DB; ++b) {
-    tof[b][0] = off_tr + tr_off<D>(b, 0, lane);
-    tof[b][1] = off_tr + tr_off<D>(b, 1, lane);
+    tof[b][0] = tr_off<D>(b, 0, lane);
+    tof[b][1] = tr_off<D>(b, 1, lane);
   }
-  // P hand-over: lane `lane` of pair `pair` exchanges 16-byte chunk ch at
-  // OFF_XP + ((pair * QB*4 + ch) * 64 + lane) * 16.
-  char* xp = smem + T::OFF_XP + (pair * T::QB * 4 * 64 + lane) * 16;
 
-  f32x16 acc2[T::DB];  // dV^T (A) or dK^T (B)
+  f32x16 accv[T::DB], acck[T::DB];  // dV^T and dK^T of this wave's keys
 #pragma unroll
-  for (int b = 0; b < T::DB; ++b) acc2[b] = f32x16{};
+  for (int b = 0; b < T::DB; ++b) accv[b] = acck[b] = f32x16{};
 
   const int Tq = (N + T::BQ - 1) / T::BQ;
   const int i0 = CAUSAL ? k0 / T::BQ : 0;
@@ -240,130 +267,123 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
     if (i + 1 < Tq) issue_loads(i + 1, stage ^ 1);
     const char* sb = smem + stage * T::STAGE;
     const int qs = i * T::BQ;
+    // only the first two steps of a causal key block straddle the diagonal
+    const bool need = CAUSAL && (i - i0 < 2);
 
-    // ---- first product: S = Q K^T (A) or dP = dO V^T (B); lane: key,
-    // element j: query 32*qb + acc_row(j).  A operands read one k step ahead.
-    f32x16 acc1[T::QB];
-#pragma unroll
-    for (int qb = 0; qb < T::QB; ++qb) acc1[qb] = f32x16{};
-    {
-      v8 a[T::QB];
-#pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb) a[qb] = *reinterpret_cast<const v8*>(sb + qb * 32 * T::RS + rof[0]);
-#pragma unroll
-      for (int st = 0; st < T::KS; ++st) {
-        v8 an[T::QB];
-        if (st + 1 < T::KS) {
-#pragma unroll
-          for (int qb = 0; qb < T::QB; ++qb)
-            an[qb] = *reinterpret_cast<const v8*>(sb + qb * 32 * T::RS + rof[st + 1]);
-        }
-#pragma unroll
-        for (int qb = 0; qb < T::QB; ++qb) acc1[qb] = mfma32(a[qb], kv[st], acc1[qb]);
-        if (st + 1 < T::KS) {
-#pragma unroll
-          for (int qb = 0; qb < T::QB; ++qb) a[qb] = an[qb];
-        }
+    f32x16 s[T::QB], pd[T::QB];  // S and dP; lane: key, element j: query 32*qb + acc_row(j)
+    v8 op[T::PS], os[T::PS];     // P and dS in the input type, MFMA B operands
+    f32x4 l4[T::QB * 4], d4[T::QB * 4];
+    float pk[T::QB][16];         // P in fp32, for dS
+    unsigned keepg[T::QB * 4];   // dropout: keep bits of 4 consecutive queries at this key
+    v8 ring[PF];
+
+    // A operand of slot u
+    auto fetch = [&](auto uc) -> v8 {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < 2 * M) {
+        constexpr int qb = u / M, st = u % H, is_dp = (u % M) / H;
+        return *reinterpret_cast<const v8*>(sb + (is_dp ? T::OFF_DO : 0) + qb * 32 * T::RS + rof[st]);
+      } else {
+        constexpr int blk = (u - 2 * M) / M, is_dk = (u % M) / H, x = u % H;
+        constexpr int ps = 2 * blk + x / T::DB, b = x % T::DB;
+        return tr_pair<E>(sb + (is_dk ? 0 : T::OFF_DO) + ps * 16 * T::RS, tof[b][0], tof[b][1]);
       }
-    }
+    };
+    // P of elements j, j+1 (j even) of block qb.  Dropout: the kept P goes
+    // to dV; its 1/(1-p) scale is applied to dV at the end.
+    auto p_pair = [&](auto qc, auto jc) {
+      constexpr int qb = decltype(qc)::value, j = decltype(jc)::value;
+      constexpr int g = j / 4, cg = qb * 4 + g;
+      const int qr = qb * 32 + 8 * g + 4 * half;
+      if constexpr (DROP && j % 4 == 0) keepg[cg] = keep_col4(dp, unsigned(qs + qr) >> 2, unsigned(key), unsigned(bh));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int e = j % 4 + t;
+        float p = exp2_fast(fmaf(s[qb][j + t], c, -l4[cg][e]));
+        if (need && key > qs + qr + e) p = 0.f;
+        pk[qb][j + t] = p;
+        if constexpr (DROP) op[qb * 2 + (j >> 3)][(j + t) & 7] = (E)(((keepg[cg] >> e) & 1u) ? p : 0.f);
+        else op[qb * 2 + (j >> 3)][(j + t) & 7] = (E)p;
+      }
+    };
+    // dS of elements j, j+1 of block qb; dropout: dP = Z * (dO V^T)
+    auto ds_pair = [&](auto qc, auto jc) {
+      constexpr int qb = decltype(qc)::value, j = decltype(jc)::value;
+      constexpr int g = j / 4, cg = qb * 4 + g;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int e = j % 4 + t;
+        float dpv = pd[qb][j + t];
+        if constexpr (DROP) dpv = ((keepg[cg] >> e) & 1u) ? dpv * dp.keep_scale : 0.f;
+        os[qb * 2 + (j >> 3)][(j + t) & 7] = (E)(pk[qb][j + t] * (dpv - d4[cg][e]));
+      }
+    };
+    auto row_of = [&](int cg) { return (cg / 4) * 32 + 8 * (cg % 4) + 4 * half; };
+    auto read_lse = [&](int qb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        l4[qb * 4 + g] = *reinterpret_cast<const f32x4*>(sb + T::OFF_LSE + row_of(qb * 4 + g) * 4);
+    };
+    auto read_d = [&](int qb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        d4[qb * 4 + g] = *reinterpret_cast<const f32x4*>(sb + T::OFF_DD + row_of(qb * 4 + g) * 4);
+    };
 
-    // ---- A: P = exp2(S*c - LSE2) (causal: keys after the query -> 0), to
-    // its partner through LDS and rounded to the input type for dV
-    v8 op[T::PS];  // P (A) or dS (B), 16-bit, MFMA B operand of the second product
-    if (role_a) {
-      // only the first two steps of a causal key block straddle the diagonal
-      const bool need = CAUSAL && (i - i0 < 2);
-#pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(sb + T::OFF_LSE + (qb * 32 + 8 * g + 4 * half) * 4);
-          f32x4 p4;
-          // dropout: the keep bits of these 4 consecutive queries at this key;
-          // a dropped element is handed over with its sign bit set (P >= 0)
-          unsigned keep = 0xFu;
-          if constexpr (DROP) keep = keep_col4(dp, unsigned(qs + qb * 32 + 8 * g + 4 * half) >> 2, unsigned(key), unsigned(bh));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float p = exp2_fast(fmaf(acc1[qb][4 * g + e], c, -l4[e]));
-            if (need && key > qs + qb * 32 + 8 * g + 4 * half + e) p = 0.f;
-            const int j = 4 * g + e;
-            if constexpr (DROP) {
-              // the kept P for dV; its 1/(1-p) scale is applied to dV at the end
-              const bool kept = (keep >> e) & 1u;
-              p4[e] = kept ? p : -p;
-              op[qb * 2 + (j >> 3)][j & 7] = (E)(kept ? p : 0.f);
-            } else {
-              p4[e] = p;
-              op[qb * 2 + (j >> 3)][j & 7] = (E)p;
-            }
-          }
-          *reinterpret_cast<f32x4*>(xp + (qb * 4 + g) * 64 * 16) = p4;
-        }
-    }
-    __syncthreads();  // P of this step is in LDS
-    // ---- B: dS = P * (dP - D), rounded to the input type
-    if (!role_a) {
-#pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(sb + T::OFF_DD + (qb * 32 + 8 * g + 4 * half) * 4);
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(xp + (qb * 4 + g) * 64 * 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 4 * g + e;
-            if constexpr (DROP) {
-              // dP = Z * (dO V^T): dropped elements (sign bit set) contribute -P*D only.
-              // The element goes through its own register first: the compiler
-              // otherwise tests the sign of element 0 for all four.
-              float pe = p4[e];
-              asm volatile("" : "+v"(pe));
-              const bool kept = !(__builtin_bit_cast(unsigned, pe) >> 31);
-              const float dpz = kept ? acc1[qb][j] * dp.keep_scale : 0.f;
-              op[qb * 2 + (j >> 3)][j & 7] = (E)(fabsf(pe) * (dpz - d4[e]));
-            } else {
-              op[qb * 2 + (j >> 3)][j & 7] = (E)(p4[e] * (acc1[qb][j] - d4[e]));
-            }
-          }
-        }
-    }
-
-    // ---- second product: dV^T += dO^T P (A) or dK^T += Q^T dS (B), k = query
-    // in the accumulator's order; transposed operands read one MFMA ahead
-    {
-      v8 a = tr_pair<E>(sb, tof[0][0], tof[0][1]);
-#pragma unroll
-      for (int ps = 0; ps < T::PS; ++ps)
-#pragma unroll
-        for (int b = 0; b < T::DB; ++b) {
-          const int nb = (b + 1 < T::DB) ? b + 1 : 0;
-          const int nps = (b + 1 < T::DB) ? ps : ps + 1;
-          v8 an;
-          if (nps < T::PS) an = tr_pair<E>(sb + nps * 16 * T::RS, tof[nb][0], tof[nb][1]);
-          acc2[b] = mfma32(a, op[ps], acc2[b]);
-          if (nps < T::PS) a = an;
-        }
-    }
+    static_for<PF>([&](auto uc) { ring[decltype(uc)::value] = fetch(uc); });
+    static_for<4 * M>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const v8 a = ring[u % PF];
+      if constexpr (u < 2 * M) {
+        constexpr int qb = u / M, st = u % H, is_dp = (u % M) / H;
+        if constexpr (!is_dp) s[qb] = mfma32(a, kf[st], st == 0 ? f32x16{} : s[qb]);
+        else pd[qb] = mfma32(a, vf[st], st == 0 ? f32x16{} : pd[qb]);
+      } else {
+        constexpr int blk = (u - 2 * M) / M, is_dk = (u % M) / H, x = u % H;
+        constexpr int ps = 2 * blk + x / T::DB, b = x % T::DB;
+        if constexpr (!is_dk) accv[b] = mfma32(a, op[ps], accv[b]);
+        else acck[b] = mfma32(a, os[ps], acck[b]);
+      }
+      if constexpr (u + PF < 4 * M) ring[u % PF] = fetch(std::integral_constant<int, u + PF>{});
+      if constexpr (u == (T::P0 >= 6 ? T::P0 - 6 : 0)) read_lse(0);
+      if constexpr (u == T::D0 - 6) read_d(0);
+      if constexpr (u == T::P1 - 6) read_lse(1);
+      if constexpr (u == T::D1 - 6) read_d(1);
+      static_for<T::PP>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        using Z = std::integral_constant<int, 0>;
+        using O = std::integral_constant<int, 1>;
+        if constexpr (u >= T::P0 && u < T::P0 + H) p_pair(Z{}, std::integral_constant<int, 2 * (T::PP * (u - T::P0) + t)>{});
+        if constexpr (u >= T::D0 && u < T::D0 + H) ds_pair(Z{}, std::integral_constant<int, 2 * (T::PP * (u - T::D0) + t)>{});
+        if constexpr (u >= T::P1 && u < T::P1 + H) p_pair(O{}, std::integral_constant<int, 2 * (T::PP * (u - T::P1) + t)>{});
+        if constexpr (u >= T::D1 && u < T::D1 + H) ds_pair(O{}, std::integral_constant<int, 2 * (T::PP * (u - T::D1) + t)>{});
+      });
+      // keep the slot order: the scheduler would otherwise pull each LDS read
+      // next to its MFMA and bunch the VALU work
+      __builtin_amdgcn_sched_barrier(0);
+    });
 
     // the loads of step i+1 have landed; every wave is done with this stage
-    // and with the P hand-over buffer
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
-  // ---- epilogue: dV = (dV^T)^T (A), dK = scale * (dK^T)^T (B); lane holds
-  // key `key`, keys past N are dropped by the buffer bounds
-  const float f = role_a ? (DROP ? dp.keep_scale : 1.f) : scale;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc((role_a ? dV : dK) + head, head_bytes);
+  // ---- epilogue: dV = (dV^T)^T (times 1/(1-p) with dropout), dK = scale * (dK^T)^T;
+  // lane holds key `key`, keys past N are dropped by the buffer bounds
+  const float fv = DROP ? dp.keep_scale : 1.f;
+  const __amdgpu_buffer_rsrc_t rvo = make_rsrc(dV + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rko = make_rsrc(dK + head, head_bytes);
 #pragma unroll
   for (int b = 0; b < T::DB; ++b)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w;
-      w[0] = pack2<E>(acc2[b][4 * g + 0] * f, acc2[b][4 * g + 1] * f);
-      w[1] = pack2<E>(acc2[b][4 * g + 2] * f, acc2[b][4 * g + 3] * f);
-      __builtin_amdgcn_raw_buffer_store_b64(w, ro, key * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
+      w[0] = pack2<E>(accv[b][4 * g + 0] * fv, accv[b][4 * g + 1] * fv);
+      w[1] = pack2<E>(accv[b][4 * g + 2] * fv, accv[b][4 * g + 3] * fv);
+      __builtin_amdgcn_raw_buffer_store_b64(w, rvo, key * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
+      w[0] = pack2<E>(acck[b][4 * g + 0] * scale, acck[b][4 * g + 1] * scale);
+      w[1] = pack2<E>(acck[b][4 * g + 2] * scale, acck[b][4 * g + 3] * scale);
+      __builtin_amdgcn_raw_buffer_store_b64(w, rko, key * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
 }
 

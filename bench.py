@@ -34,6 +34,7 @@ from aware_exact_attention_amd.inputs import WORKLOADS, make_inputs, to_f64  # n
 
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak at B1 H8 N16K d128; bwd TFLOP/s"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector (the f32 path runs on the vector ALUs)
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "aware_exact_attention_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_traffic_B1H8N16384d128.txt")
@@ -177,6 +178,39 @@ def _graph_ms(fn, calls: int, warmup: int = 3) -> float:
         torch.cuda.synchronize()
         rounds.append(e0.elapsed_time(e1) / calls)
     return sorted(rounds)[len(rounds) // 2]
+
+
+def config_rows():
+    """Every configuration of the task at its own shape: forward (and, for the
+    forward+backward config, backward) time, TFLOP/s and fraction of the bf16
+    peak; the sequence-length sweep per N.  Graph-replayed calls."""
+    res = {}
+    for name in ("tiny_f32", "gpt2", "gpt2_causal", "sweep_2k", "sweep_4k", "sweep_8k", "sweep_16k",
+                 "stress_causal", "fwd_bwd_causal"):
+        w = WORKLOADS[name]
+        ts = make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_std, backward=w.backward)
+        q, k, v = (t.cuda() for t in ts[:3])
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+        # enough calls per replay (about 20 ms of work at the large shapes) that
+        # the clock has settled after the host-side input generation
+        calls = max(3, min(50, int(2e13 / max(w.fwd_flop, 1))))
+        t_f = _graph_ms(lambda: fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse), calls)
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        r = {"shape": [w.B, w.H, w.N, w.d], "dtype": w.dtype, "causal": w.causal,
+             "peak_tflops": peak,
+             "fwd_ms": round(t_f, 5), "fwd_tflops": round(w.fwd_flop / (t_f * 1e-3) / 1e12, 1),
+             "fwd_frac_peak": round(w.fwd_flop / (t_f * 1e-3) / 1e12 / peak, 4)}
+        if w.backward:
+            do = ts[3].cuda()
+            grads = tuple(torch.empty_like(q) for _ in range(3))
+            ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+            t_b = _graph_ms(lambda: fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws,
+                                           out=grads), max(3, min(50, int(2e13 / w.bwd_flop))))
+            r.update({"bwd_ms": round(t_b, 5), "bwd_tflops": round(w.bwd_flop / (t_b * 1e-3) / 1e12, 1),
+                      "bwd_frac_peak": round(w.bwd_flop / (t_b * 1e-3) / 1e12 / peak, 4)})
+        res[name] = r
+    return res
 
 
 def next_rows():
@@ -368,6 +402,7 @@ def main():
         "roofline_fwd": r_fwd,
     }
     if not a.no_next_rows:
+        out["configs"] = config_rows()
         out["next_rows"] = next_rows()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, a.cpu_heads)
