@@ -299,8 +299,7 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int e = j % 4 + t;
-        float p = exp2_fast(fmaf(s[qb][j + t], c, -l4[cg][e]));
-        if (need && key > qs + qr + e) p = 0.f;
+        const float p = exp2_fast(fmaf(s[qb][j + t], c, -l4[cg][e]));
         pk[qb][j + t] = p;
         if constexpr (DROP) op[qb * 2 + (j >> 3)][(j + t) & 7] = (E)(((keepg[cg] >> e) & 1u) ? p : 0.f);
         else op[qb * 2 + (j >> 3)][(j + t) & 7] = (E)p;
@@ -345,6 +344,17 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
         else acck[b] = mfma32(a, os[ps], acck[b]);
       }
       if constexpr (u + PF < 4 * M) ring[u % PF] = fetch(std::integral_constant<int, u + PF>{});
+      // causal: S = -inf (P = 0) where the key is after the query, on the
+      // steps that straddle the diagonal only (a wave-uniform branch)
+      if constexpr (CAUSAL && (u == T::P0 - 1 || u == T::P1 - 1)) {
+        constexpr int qb = u == T::P0 - 1 ? 0 : 1;
+        if (need) {
+          const int t = key - qs - 4 * half;  // key > qs + qb*32 + acc_row(j) <=> t > qb*32 + 8*(j/4) + j%4
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (t > qb * 32 + 8 * (j >> 2) + (j & 3)) s[qb][j] = -INFINITY;
+        }
+      }
       if constexpr (u == (T::P0 >= 6 ? T::P0 - 6 : 0)) read_lse(0);
       if constexpr (u == T::D0 - 6) read_d(0);
       if constexpr (u == T::P1 - 6) read_lse(1);
@@ -539,8 +549,18 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
     // ---- dS^T = P^T * (dP^T - D) with P^T = exp2(S^T*c - LSE2), rounded to the input type.
     // Keys past N have zero K and V rows, so they add nothing to dQ; causal
     // keys after the query are masked on the tiles that straddle the diagonal.
+    // causal keys after the query: S^T = -inf (P = 0) on the tiles that
+    // straddle the diagonal for some query of the wave (a wave-uniform branch)
     const int key0 = j * T::BC;
-    const bool need = CAUSAL && (key0 + T::BC - 1 > wq0);
+    if (CAUSAL && key0 + T::BC - 1 > wq0) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+        const int t = qrow - key0 - kb * 32 - 4 * half;  // key > qrow <=> 8*(r/4) + r%4 > t
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
+      }
+    }
     v8 db[T::PS];
     // dropout: registers 4m .. 4m+3 of a key block hold 4 consecutive keys of
     // this lane's query, one Philox block row; dP = Z * (dO V^T)
@@ -557,8 +577,7 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = exp2_fast(fmaf(s[kb][r], c, -lq));
-        if (need && key0 + kb * 32 + acc_row(r, lane) > qrow) pr = 0.f;
+        const float pr = exp2_fast(fmaf(s[kb][r], c, -lq));
         float dpv = p[kb][r];
         if constexpr (DROP) dpv = ((keep >> (kb * 16 + r)) & 1u) ? dpv * dp.keep_scale : 0.f;
         db[kb * 2 + (r >> 3)][r & 7] = (E)(pr * (dpv - dd));
@@ -631,11 +650,12 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
 
   const int Tk = (N + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV;
   const long long Gk = (long long)B * H * Tk;
-  // dQ pass: eight waves (256 rows) per workgroup for non-causal d = 128 grids
-  // that cover every CU (each K/V tile streamed once for twice the rows), as
-  // in the forward; four waves otherwise.
+  // dQ pass: eight waves (256 rows) per workgroup for d = 128 grids that cover
+  // every CU (each K/V tile streamed once for twice the rows); four waves
+  // otherwise.  Unlike the forward, the causal dQ pass gains from eight waves
+  // too (1-2 % at B4 H16 N4096 and B2 H8 N16000).
   const long long Gq8 = (long long)B * H * ((N + DqTile<D, 8>::BR - 1) / DqTile<D, 8>::BR);
-  const bool dq8 = D == 128 && !CAUSAL && Gq8 >= kNumCUs;
+  const bool dq8 = D == 128 && Gq8 >= kNumCUs;
   const int Tr = dq8 ? (N + DqTile<D, 8>::BR - 1) / DqTile<D, 8>::BR : (N + DqTile<D, 4>::BR - 1) / DqTile<D, 4>::BR;
   const long long Gq = (long long)B * H * Tr;
   if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
