@@ -431,10 +431,16 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / Tr;
-  int it = tile - bh * Tr;
-  if (CAUSAL) it = Tr - 1 - it;  // longest rows first
+  int bh, it;
+  if (CAUSAL) {
+    int r;
+    causal_order(blockIdx.x, gridDim.x / Tr, Tr, bh, r);
+    it = Tr - 1 - r;  // longest rows first
+  } else {
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    bh = tile / Tr;
+    it = tile - bh * Tr;
+  }
   const int q0 = it * T::BR;
   const size_t head = size_t(bh) * N * D;
   const E* Kh = K + head;

@@ -216,6 +216,26 @@ __device__ __forceinline__ int xcd_remap(int w, int G) {
   return (w & 7) * (G >> 3) + (w >> 3);
 }
 
+// Causal query-major grids (BH heads x T row blocks, block rank r of a head
+// has T - r key tiles): block w -> (head bh, rank r, 0 = the head's longest).
+// When BH is a multiple of the 8 XCDs, XCD x = w % 8 takes the heads
+// bh = x (mod 8) -- their K and V stay in that XCD's L2 -- and dispatches
+// its blocks longest first over all of those heads, so that the short blocks
+// of every head fill in at the end.  (Head by head, each XCD would start a
+// new head's long blocks while its other CUs run short ones, and finish
+// unevenly.)  Otherwise: xcd_remap order, longest first within a head.
+__device__ __forceinline__ void causal_order(int w, int BH, int T, int& bh, int& r) {
+  if ((BH & 7) == 0) {
+    const int x = w & 7, k = w >> 3, hp = BH >> 3;
+    r = k / hp;
+    bh = x + 8 * (k - r * hp);
+  } else {
+    const int t = xcd_remap(w, BH * T);
+    bh = t / T;
+    r = t - bh * T;
+  }
+}
+
 }  // namespace fa
 
 #endif  // FA_COMMON_H_

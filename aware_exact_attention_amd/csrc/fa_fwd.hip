@@ -100,13 +100,20 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int per_head = SPLIT ? Tr * sp.S : Tr;  // the parts of a query block are adjacent
-  const int bh = tile / per_head;
-  const int rem = tile - bh * per_head;
-  const int part = SPLIT ? rem % sp.S : 0;
-  int it = SPLIT ? rem / sp.S : rem;
-  if (CAUSAL) it = Tr - 1 - it;  // longest rows first
+  int bh, it, part = 0;
+  if (CAUSAL && !SPLIT) {
+    int r;
+    causal_order(blockIdx.x, gridDim.x / Tr, Tr, bh, r);
+    it = Tr - 1 - r;  // longest rows first
+  } else {
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    bh = tile / per_head;
+    const int rem = tile - bh * per_head;
+    part = SPLIT ? rem % sp.S : 0;
+    it = SPLIT ? rem / sp.S : rem;
+    if (CAUSAL) it = Tr - 1 - it;  // longest rows first
+  }
   const int q0 = it * T::BR;
   const size_t head = size_t(bh) * N * D;
   const E* Kh = K + head;
