@@ -184,7 +184,7 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses for the direct loads
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -428,7 +428,7 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses for the direct loads
   const int half = lane >> 5;
   const int l32 = lane & 31;
   int bh, it;

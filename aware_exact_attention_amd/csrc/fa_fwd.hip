@@ -97,7 +97,7 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses for the direct loads
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int per_head = SPLIT ? Tr * sp.S : Tr;  // the parts of a query block are adjacent
