@@ -38,8 +38,6 @@
 #include "fa_common.h"
 #include "fa_validate.h"
 
-#include <utility>
-
 namespace fa {
 
 // Byte offset, inside a row-major tile with rows of 2*DD bytes swizzled by
@@ -159,17 +157,6 @@ struct DkdvTile {
   // first slots of: P of block 0, dS of block 0, P of block 1, dS of block 1
   static constexpr int P0 = H + 2, D0 = 2 * H + 1, P1 = 3 * H + 2, D1 = 4 * H + 1;
 };
-
-// Calls f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{})
-// in order, so that every index inside f is a compile-time constant.
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_seq(f, std::make_integer_sequence<int, N>{});
-}
 
 template <typename E, int D, bool CAUSAL, bool DROP>
 __global__ void __launch_bounds__(256, 1)

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <utility>
 
 namespace fa {
 
@@ -205,6 +206,17 @@ __device__ __forceinline__ unsigned keep_col4(const DropArgs& dp, unsigned i4, u
 #pragma unroll
   for (int e = 0; e < 4; ++e) bits |= unsigned(((w[e] >> sh) & 0xFFu) >= dp.t) << e;
   return bits;
+}
+
+// Calls f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{})
+// in order, so that every index inside f is a compile-time constant.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // Map a linear workgroup id to a tile id so that the tiles of one (b, h)

@@ -21,6 +21,12 @@ Within the visible set the computation is the plain definition of
 ``oracle/ref.py``.  A row with no visible key (possible only with a block
 mask) has an empty softmax; its output is taken as ``O = 0`` and its
 log-sum-exp as ``-inf`` (the sum over an empty set is 0).
+
+The backward under a mask is the chain rule on that forward, as for the dense
+case (recompute P, then dV = P^T dO, dP = dO V^T, dS = P * (dP - D) with
+D_i = sum_j P_ij dP_ij, dQ = scale dS K, dK = scale dS^T Q): hidden entries
+have P = 0 and so add nothing, and a row with no visible key has a constant
+output O = 0, so it contributes nothing to any gradient and its dQ row is 0.
 """
 from __future__ import annotations
 
@@ -132,3 +138,52 @@ def ref_fwd_blocksparse_rows(q, k, v, scale: float, causal: bool, block_mask, ro
     if causal:
         vis &= np.arange(k.shape[0])[None, :] <= rows[:, None]
     return _rows_fwd(q[rows], k, v, scale, vis)
+
+
+def _visible_probs(q, k, scale: float, vis):
+    """One head: ``P [R, N]`` of the query rows whose visibility rows are ``vis``; empty rows are 0."""
+    s = np.where(vis, scale * (q @ k.T), -np.inf)
+    m = s.max(axis=1)
+    p = np.zeros_like(s)
+    seen = m > -np.inf
+    if seen.any():
+        f = np.exp(s[seen] - m[seen, None])
+        p[seen] = f / f.sum(axis=1, keepdims=True)
+    return p
+
+
+def _grads_from_probs(p, q, k, v, do, scale: float):
+    """Chain rule of one head from its probabilities: ``(dQ, dK, dV)``."""
+    dv = p.T @ do
+    dp = do @ v.T
+    D = (p * dp).sum(axis=1, keepdims=True)
+    ds = p * (dp - D)
+    return scale * (ds @ k), scale * (ds.T @ q), dv
+
+
+def ref_bwd_visible(q, k, v, do, scale: float, visible):
+    """Gradients ``(dQ, dK, dV)`` of ``sum(O * dO)`` for ``ref_fwd_visible``'s attention, float64."""
+    q, k, v, do = _as_f64(q, k, v, do)
+    B, H, _, _ = q.shape
+    visible = np.asarray(visible, dtype=bool)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for b in range(B):
+        for h in range(H):
+            vis = visible if visible.ndim == 2 else visible[h]
+            p = _visible_probs(q[b, h], k[b, h], scale, vis)
+            dq[b, h], dk[b, h], dv[b, h] = _grads_from_probs(p, q[b, h], k[b, h], v[b, h], do[b, h], scale)
+    return dq, dk, dv
+
+
+def ref_bwd_window(q, k, v, do, scale: float, left: int, right: int):
+    """Gradients of sliding-window attention (the window read as in ``window_visible``)."""
+    return ref_bwd_visible(q, k, v, do, scale, window_visible(np.shape(q)[2], left, right))
+
+
+def ref_bwd_blocksparse(q, k, v, do, scale: float, causal: bool, block_mask):
+    """Gradients of block-sparse attention; ``block_mask`` is ``[nb,nb]`` or ``[H,nb,nb]``."""
+    N = np.shape(q)[2]
+    bm = np.asarray(block_mask)
+    if bm.ndim == 2:
+        return ref_bwd_visible(q, k, v, do, scale, blocksparse_visible(N, bm, causal))
+    return ref_bwd_visible(q, k, v, do, scale, np.stack([blocksparse_visible(N, m, causal) for m in bm]))
