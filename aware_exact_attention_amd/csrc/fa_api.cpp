@@ -34,6 +34,13 @@ hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* 
 hipError_t launch_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                   int N, int d, float scale, int causal, const unsigned char* bm, int per_head,
                                   hipStream_t st);
+hipError_t launch_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                             int left, int right, void* ws, hipStream_t st);
+hipError_t launch_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                  const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                                  float scale, int causal, const unsigned char* bm, int per_head, void* ws,
+                                  hipStream_t st);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                       int causal, void* ws, hipStream_t st);
@@ -212,6 +219,36 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
   if (st != fa::kOk) return st;
   return fa::launch_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, mask_per_head,
                                     stream) == hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                  void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int window_left,
+                  int window_right, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, s, scale, workspace, workspace_bytes);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, window_left, window_right,
+                               workspace, stream) == hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                       int causal, const unsigned char* block_mask, int mask_per_head, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, block_mask,
+                                        mask_per_head, workspace, workspace_bytes);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, block_mask,
+                                    mask_per_head, workspace, stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
 }

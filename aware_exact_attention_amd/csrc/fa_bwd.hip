@@ -80,7 +80,7 @@ __device__ __forceinline__ int swz_src(int p) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O) and LSE2 = LSE * log2(e).  8 lanes per row.
+// 1. D = rowsum(dO * O) and LSE2 = LSE * log2(e) (+inf for LSE = -inf).  8 lanes per row.
 // ---------------------------------------------------------------------------
 template <typename E, int D>
 __global__ void __launch_bounds__(256)
@@ -108,7 +108,10 @@ bwd_pre_kernel(const E* __restrict__ O, const E* __restrict__ dO, const float* _
   acc += __shfl_xor(acc, 4);
   if (row < rows && sub == 0) {
     Dv[row] = acc;
-    lse2[row] = LSE[row] * kLog2e;
+    // a row that saw no key (LSE = -inf, block-sparse masks only) gets +inf,
+    // so that P = exp2(S*c - LSE2) = 0 for every key, masked (-inf) or not
+    const float l = LSE[row];
+    lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
@@ -158,16 +161,21 @@ struct DkdvTile {
   static constexpr int P0 = H + 2, D0 = 2 * H + 1, P1 = 3 * H + 2, D1 = 4 * H + 1;
 };
 
-template <typename E, int D, bool CAUSAL, bool DROP>
+template <typename E, int D, bool CAUSAL, bool DROP, int MODE>
 __global__ void __launch_bounds__(256, 1)
 bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
                 const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
                 E* __restrict__ dK, E* __restrict__ dV, DropArgs dp, int N, int Tk, float c /* scale*log2(e) */,
-                float scale) {
+                float scale, MaskArgs mk) {
   using T = DkdvTile<D>;
   using v8 = typename Vec<E>::v8;
   constexpr int M = T::M, H = T::H, PF = T::PF;
+  constexpr bool WINDOW = MODE == kMaskWindow, BLOCKS = MODE == kMaskBlocks;
+  static_assert(!(DROP && MODE != kMaskDense), "dropout only with the dense or causal mask");
+  static_assert(!BLOCKS || (T::BQ == kMaskBlock && T::BKV == 2 * kMaskBlock), "query steps are mask blocks");
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
+  __shared__ unsigned short slist[BLOCKS ? kMaxMaskTiles : 1];
+  __shared__ int scount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -243,19 +251,57 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
   for (int b = 0; b < T::DB; ++b) accv[b] = acck[b] = f32x16{};
 
   const int Tq = (N + T::BQ - 1) / T::BQ;
-  const int i0 = CAUSAL ? k0 / T::BQ : 0;
+  // this workgroup's query steps: [i0, i1), or (block-sparse) the steps
+  // slist[0 .. scount) whose 64-query block keeps one of its two key blocks
+  int i0 = CAUSAL ? k0 / T::BQ : 0, i1 = Tq;
+  if (WINDOW) {
+    // queries i with i - left <= key <= i + right for a key of the workgroup
+    if (mk.right >= 0) i0 = max(0, k0 - mk.right) / T::BQ;
+    if (mk.left >= 0) i1 = (int)min((long long)N - 1, (long long)k0 + T::BKV - 1 + mk.left) / T::BQ + 1;
+  }
+  const int kw0 = k0 + wave * 32;  // this wave's first key
+  const unsigned char* bm_col = nullptr;  // this wave's key block, row stride nb
+  if (BLOCKS) {
+    const unsigned char* bmh = mk.bm + mk.bm_head_stride * (bh % mk.H);
+    const int kb0 = k0 / kMaskBlock;
+    const bool two = kb0 + 1 < mk.nb;
+    bm_col = bmh + min(kw0, N - 1) / kMaskBlock;
+    if (wave == 0) {
+      int n = 0;
+      for (int base = i0; base < Tq; base += 64) {
+        const int ii = base + lane;
+        const bool keep = ii < Tq && (bmh[size_t(ii) * mk.nb + kb0] != 0 || (two && bmh[size_t(ii) * mk.nb + kb0 + 1] != 0));
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(keep);
+        const int below = __builtin_popcountll(bal & ((1ull << lane) - 1));
+        if (keep) slist[n + below] = (unsigned short)ii;
+        n += __builtin_popcountll(bal);
+      }
+      if (lane == 0) scount = n;
+    }
+    __syncthreads();
+  }
+  const int cnt = BLOCKS ? scount : i1 - i0;
+  auto step_at = [&](int idx) { return BLOCKS ? int(slist[idx]) : i0 + idx; };
 
-  issue_loads(i0, 0);
+  if (cnt > 0) {  // uniform over the workgroup; a key block no query sees only stores zeros
+  issue_loads(step_at(0), 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
-  for (int i = i0; i < Tq; ++i) {
-    const int stage = (i - i0) & 1;
-    if (i + 1 < Tq) issue_loads(i + 1, stage ^ 1);
+  for (int idx = 0; idx < cnt; ++idx) {
+    const int i = step_at(idx);
+    const int stage = idx & 1;
+    if (idx + 1 < cnt) issue_loads(step_at(idx + 1), stage ^ 1);
     const char* sb = smem + stage * T::STAGE;
     const int qs = i * T::BQ;
-    // only the first two steps of a causal key block straddle the diagonal
-    const bool need = CAUSAL && (i - i0 < 2);
+    // steps whose element mask matters for this wave's keys: causal, the two
+    // steps that straddle the diagonal; a window edge inside the step; a
+    // block that drops this wave's keys
+    bool need = CAUSAL && kw0 + 31 > qs;
+    if (WINDOW)
+      need = need || (mk.left >= 0 && kw0 < qs + T::BQ - 1 - mk.left) || (mk.right >= 0 && kw0 + 31 > qs + mk.right);
+    const bool dead = BLOCKS && bm_col[size_t(i) * mk.nb] == 0;
+    if (BLOCKS) need = need || dead;
 
     f32x16 s[T::QB], pd[T::QB];  // S and dP; lane: key, element j: query 32*qb + acc_row(j)
     v8 op[T::PS], os[T::PS];     // P and dS in the input type, MFMA B operands
@@ -331,15 +377,20 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
         else acck[b] = mfma32(a, os[ps], acck[b]);
       }
       if constexpr (u + PF < 4 * M) ring[u % PF] = fetch(std::integral_constant<int, u + PF>{});
-      // causal: S = -inf (P = 0) where the key is after the query, on the
-      // steps that straddle the diagonal only (a wave-uniform branch)
-      if constexpr (CAUSAL && (u == T::P0 - 1 || u == T::P1 - 1)) {
+      // masks: S = -inf (P = 0) where the key is after the query (causal),
+      // outside the query's window, or in a dropped block, on the steps that
+      // need it only (a wave-uniform branch)
+      if constexpr ((CAUSAL || MODE != kMaskDense) && (u == T::P0 - 1 || u == T::P1 - 1)) {
         constexpr int qb = u == T::P0 - 1 ? 0 : 1;
         if (need) {
-          const int t = key - qs - 4 * half;  // key > qs + qb*32 + acc_row(j) <=> t > qb*32 + 8*(j/4) + j%4
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (t > qb * 32 + 8 * (j >> 2) + (j & 3)) s[qb][j] = -INFINITY;
+          for (int j = 0; j < 16; ++j) {
+            const int qj = qs + qb * 32 + acc_row(j, lane);
+            bool hide = CAUSAL && key > qj;
+            if (WINDOW) hide = hide || window_hides(mk, qj, key);
+            if (BLOCKS) hide = hide || dead;
+            if (hide) s[qb][j] = -INFINITY;
+          }
         }
       }
       if constexpr (u == (T::P0 >= 6 ? T::P0 - 6 : 0)) read_lse(0);
@@ -363,6 +414,7 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
     // the loads of step i+1 have landed; every wave is done with this stage
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
+  }
   }
 
   // ---- epilogue: dV = (dV^T)^T (times 1/(1-p) with dropout), dK = scale * (dK^T)^T;
@@ -404,14 +456,20 @@ struct DqTile {
   static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
 };
 
-template <typename E, int D, bool CAUSAL, int NW, bool DROP>
+template <typename E, int D, bool CAUSAL, int NW, bool DROP, int MODE>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
 bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
               const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
-              E* __restrict__ dQ, DropArgs dp, int N, int Tr, float c /* scale*log2(e) */, float scale) {
+              E* __restrict__ dQ, DropArgs dp, int N, int Tr, float c /* scale*log2(e) */, float scale,
+              MaskArgs mk) {
   using T = DqTile<D, NW>;
   using v8 = typename Vec<E>::v8;
+  constexpr bool WINDOW = MODE == kMaskWindow, BLOCKS = MODE == kMaskBlocks;
+  static_assert(!(DROP && MODE != kMaskDense), "dropout only with the dense or causal mask");
+  static_assert(!BLOCKS || (T::BC == kMaskBlock && T::BR == 2 * kMaskBlock), "mask blocks are key tiles and half a row block");
   __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+  __shared__ unsigned short tlist[BLOCKS ? kMaxMaskTiles : 1];
+  __shared__ int tcount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -462,6 +520,44 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
   const bool wave_active = wq0 < N;
   int nt_w = nt;
   if (CAUSAL && wave_active) nt_w = min(nt, (min(wq0 + 32, N) - 1) / T::BC + 1);
+  // this workgroup's key tiles: [j0, nt), or (block-sparse) tlist[0 .. tcount);
+  // each wave computes the tiles of [w0, nt_w) (block-sparse: those its own
+  // 64-row block keeps)
+  int j0 = 0, w0 = 0;
+  if (WINDOW) {
+    const int lo = mk.left >= 0 ? max(0, q0 - mk.left) : 0;
+    const int hi = mk.right >= 0 ? (int)min((long long)N, (long long)q0 + T::BR + mk.right) : N;  // exclusive
+    j0 = lo / T::BC;
+    nt = (hi - 1) / T::BC + 1;
+    w0 = mk.left >= 0 ? max(0, wq0 - mk.left) / T::BC : 0;
+    nt_w = mk.right >= 0 ? (int)((min((long long)N, (long long)wq0 + 32 + mk.right) - 1) / T::BC + 1) : Tc;
+  }
+  const unsigned char* bm_row = nullptr;
+  if (BLOCKS) {
+    const unsigned char* bmh = mk.bm + mk.bm_head_stride * (bh % mk.H);
+    bm_row = bmh + size_t(min(wq0, N - 1) / kMaskBlock) * mk.nb;
+    if (wave == 0) {
+      const unsigned char* r0 = bmh + size_t(q0 / kMaskBlock) * mk.nb;
+      const bool two = q0 + kMaskBlock < N;
+      int n = 0;
+      for (int base = 0; base < nt; base += 64) {
+        const int jj = base + lane;
+        const bool keep = jj < nt && (r0[jj] != 0 || (two && r0[mk.nb + jj] != 0));
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(keep);
+        const int below = __builtin_popcountll(bal & ((1ull << lane) - 1));
+        if (keep) tlist[n + below] = (unsigned short)jj;
+        n += __builtin_popcountll(bal);
+      }
+      if (lane == 0) tcount = n;
+    }
+    __syncthreads();
+  }
+  const int cnt = BLOCKS ? tcount : nt - j0;
+  auto tile_at = [&](int idx) { return BLOCKS ? int(tlist[idx]) : j0 + idx; };
+  auto wave_needs = [&](int j) {
+    if (!wave_active || j >= nt_w || j < w0) return false;
+    return !BLOCKS || bm_row[j] != 0;
+  };
 
   int goff[T::LPW];
 #pragma unroll
@@ -544,6 +640,7 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
     // keys after the query are masked on the tiles that straddle the diagonal.
     // causal keys after the query: S^T = -inf (P = 0) on the tiles that
     // straddle the diagonal for some query of the wave (a wave-uniform branch)
+    // Window edges inside the tile: keys outside [qrow - left, qrow + right].
     const int key0 = j * T::BC;
     if (CAUSAL && key0 + T::BC - 1 > wq0) {
 #pragma unroll
@@ -553,6 +650,13 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
       }
+    }
+    if (WINDOW && ((mk.left >= 0 && key0 < wq0 + 31 - mk.left) || (mk.right >= 0 && key0 + T::BC - 1 > wq0 + mk.right))) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (window_hides(mk, qrow, key0 + kb * 32 + acc_row(r, lane))) s[kb][r] = -INFINITY;
     }
     v8 db[T::PS];
     // dropout: registers 4m .. 4m+3 of a key block hold 4 consecutive keys of
@@ -590,22 +694,26 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
       }
   };
 
-  auto step = [&](int j, int stage) {
-    if (j + 1 < nt) issue_loads(j + 1, stage ^ 1);
-    if (wave_active && j < nt_w) compute(j, smem + stage * T::STAGE);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j+1 have landed
+  // step idx: tile tile_at(idx) from stage `stage`, loads of the next tile into the other
+  auto step = [&](int idx, int stage) {
+    if (idx + 1 < cnt) issue_loads(tile_at(idx + 1), stage ^ 1);
+    const int j = tile_at(idx);
+    if (wave_needs(j)) compute(j, smem + stage * T::STAGE);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the next tile have landed
     __syncthreads();
   };
 
-  issue_loads(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  int j = 0;
-  for (; j + 1 < nt; j += 2) {
-    step(j, 0);
-    step(j + 1, 1);
+  if (cnt > 0) {  // uniform over the workgroup
+    issue_loads(tile_at(0), 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    int idx = 0;
+    for (; idx + 1 < cnt; idx += 2) {
+      step(idx, 0);
+      step(idx + 1, 1);
+    }
+    if (idx < cnt) step(idx, 0);
   }
-  if (j < nt) step(j, 0);
 
   if (!wave_active) return;
   // dQ = scale * (dQ^T)^T; lane holds query qrow, rows past N are dropped by the buffer bounds
@@ -652,19 +760,19 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   const int Tr = dq8 ? (N + DqTile<D, 8>::BR - 1) / DqTile<D, 8>::BR : (N + DqTile<D, 4>::BR - 1) / DqTile<D, 4>::BR;
   const long long Gq = (long long)B * H * Tr;
   if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, DROP>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
-                     (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
-                     (const float*)lse2, (const float*)Dv, (E*)dk, (E*)dv, dp, N, Tk, c, scale);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, DROP, kMaskDense>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0,
+                     st, (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
+                     (const float*)lse2, (const float*)Dv, (E*)dk, (E*)dv, dp, N, Tk, c, scale, MaskArgs{});
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dq8)
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 8, DROP>), dim3((unsigned)Gq), dim3(DqTile<D, 8>::NT), 0, st,
-                       (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
-                       (const float*)lse2, (const float*)Dv, (E*)dq, dp, N, Tr, c, scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 8, DROP, kMaskDense>), dim3((unsigned)Gq), dim3(DqTile<D, 8>::NT),
+                       0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
+                       (const float*)lse2, (const float*)Dv, (E*)dq, dp, N, Tr, c, scale, MaskArgs{});
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 4, DROP>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT), 0, st,
-                       (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
-                       (const float*)lse2, (const float*)Dv, (E*)dq, dp, N, Tr, c, scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 4, DROP, kMaskDense>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT),
+                       0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
+                       (const float*)lse2, (const float*)Dv, (E*)dq, dp, N, Tr, c, scale, MaskArgs{});
   return hipGetLastError();
 }
 
@@ -694,6 +802,67 @@ hipError_t launch_bwd_dropout(const void* q, const void* k, const void* v, const
                   : launch_bwd_t<__bf16, 128, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
   return causal ? launch_bwd_t<__bf16, 64, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
                 : launch_bwd_t<__bf16, 64, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
+}
+
+// Sliding-window and block-sparse backward (bf16): the dense passes with a
+// per-step predicate in the dK/dV pass and a per-tile one in the dQ pass
+// (four-wave workgroups: 128 queries, two 64-row mask blocks).
+template <int D, bool CAUSAL, int MODE>
+static hipError_t launch_bwd_masked_t(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                      const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
+                                      const MaskArgs& mk, void* ws, hipStream_t st) {
+  using E = __bf16;
+  const long long rows = (long long)B * H * N;
+  const BwdWorkspace w = bwd_workspace_layout(Shape{B, H, N, D});
+  char* base = reinterpret_cast<char*>(ws);
+  float* Dv = reinterpret_cast<float*>(base + w.d);
+  float* lse2 = reinterpret_cast<float*>(base + w.lse2);
+  const float c = scale * kLog2e;
+  const long long pre_blocks = (rows * 8 + 255) / 256;
+  hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((unsigned)pre_blocks), dim3(256), 0, st,
+                     (const E*)o, (const E*)dO, lse, Dv, lse2, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int Tk = (N + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV;
+  const int Tr = (N + DqTile<D, 4>::BR - 1) / DqTile<D, 4>::BR;
+  const long long Gk = (long long)B * H * Tk, Gq = (long long)B * H * Tr;
+  if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, false, MODE>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
+                     (const E*)q, (const E*)k, (const E*)v, (const E*)dO, (const float*)lse2, (const float*)Dv,
+                     (E*)dk, (E*)dv, DropArgs{}, N, Tk, c, scale, mk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 4, false, MODE>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT), 0, st,
+                     (const E*)q, (const E*)k, (const E*)v, (const E*)dO, (const float*)lse2, (const float*)Dv,
+                     (E*)dq, DropArgs{}, N, Tr, c, scale, mk);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                             int left, int right, void* ws, hipStream_t st) {
+  // a bound of N - 1 or more limits nothing: the same as no bound
+  const MaskArgs mk{left >= N - 1 ? -1 : left, right >= N - 1 ? -1 : right, nullptr, 0, 0, H};
+  if (d == 128)
+    return launch_bwd_masked_t<128, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
+  return launch_bwd_masked_t<64, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
+}
+
+hipError_t launch_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                  const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                                  float scale, int causal, const unsigned char* bm, int per_head, void* ws,
+                                  hipStream_t st) {
+  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+  const MaskArgs mk{-1, -1, bm, per_head ? (long long)nb * nb : 0, nb, H};
+  if (d == 128)
+    return causal ? launch_bwd_masked_t<128, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                                 ws, st)
+                  : launch_bwd_masked_t<128, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                                  ws, st);
+  return causal ? launch_bwd_masked_t<64, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws,
+                                                              st)
+                : launch_bwd_masked_t<64, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                               ws, st);
 }
 
 hipError_t launch_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,

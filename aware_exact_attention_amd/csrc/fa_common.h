@@ -208,6 +208,26 @@ __device__ __forceinline__ unsigned keep_col4(const DropArgs& dp, unsigned i4, u
   return bits;
 }
 
+// Tile-skipping masks (beyond causal), shared by the forward and backward.
+// kMaskWindow: key j is visible to query i iff i - left <= j <= i + right (a
+// negative bound: no limit on that side).  kMaskBlocks: bm[h][i / 64][j / 64] != 0 keeps the 64 x 64 block,
+// with the causal mask on top when CAUSAL; bm_head_stride is 0 when all
+// heads share one mask.
+enum : int { kMaskDense = 0, kMaskWindow = 1, kMaskBlocks = 2 };
+constexpr int kMaskBlock = 64;
+constexpr int kMaxMaskTiles = 1024;  // block-sparse: N <= 65536
+struct MaskArgs {
+  int left, right;
+  const unsigned char* bm;
+  long long bm_head_stride;
+  int nb, H;
+};
+
+// Whether the window hides key `key` from query `q`.
+__device__ __forceinline__ bool window_hides(const MaskArgs& mk, int q, int key) {
+  return (mk.left >= 0 && key < q - mk.left) || (mk.right >= 0 && key > q + mk.right);
+}
+
 // Calls f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{})
 // in order, so that every index inside f is a compile-time constant.
 template <typename F, int... Is>

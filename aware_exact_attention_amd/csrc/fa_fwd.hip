@@ -65,20 +65,6 @@ struct SplitArgs {
   long long part_elems, part_rows;  // B*H*N*d and B*H*N
 };
 
-// Tile-skipping masks (beyond causal).  kMaskWindow: key j is visible to
-// query i iff i - left <= j <= i + right (a negative bound: no limit on that
-// side).  kMaskBlocks: bm[h][i / 64][j / 64] != 0 keeps the 64 x 64 block,
-// with the causal mask on top when CAUSAL; bm_head_stride is 0 when all
-// heads share one mask.
-enum : int { kMaskDense = 0, kMaskWindow = 1, kMaskBlocks = 2 };
-constexpr int kMaskBlock = 64;
-constexpr int kMaxMaskTiles = 1024;  // block-sparse: N <= 65536
-struct MaskArgs {
-  int left, right;
-  const unsigned char* bm;
-  long long bm_head_stride;
-  int nb, H;
-};
 
 template <typename E, int D, bool CAUSAL, int NW, bool SPLIT, int MODE, bool DROP>
 __global__ void __launch_bounds__(64 * NW, 8 / NW)
@@ -706,7 +692,8 @@ static hipError_t launch_fwd_masked_t(const void* q, const void* k, const void* 
 
 hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
                              int d, float scale, int left, int right, hipStream_t st) {
-  const MaskArgs mk{left, right, nullptr, 0, 0, H};
+  // a bound of N - 1 or more limits nothing: the same as no bound
+  const MaskArgs mk{left >= N - 1 ? -1 : left, right >= N - 1 ? -1 : right, nullptr, 0, 0, H};
   if (d == 128) return launch_fwd_masked_t<128, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
   return launch_fwd_masked_t<64, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
 }

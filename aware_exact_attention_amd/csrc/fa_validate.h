@@ -246,6 +246,33 @@ inline int validate_fwd_blocksparse(const void* q, const void* k, const void* v,
 }
 
 // Dropout probability: finite, 0 <= p < 1.
+// The masked backward: fa_bwd's preconditions (without the causal flag for
+// the window) plus, for a block mask, those of fa_fwd_blocksparse on the mask
+// and no overlap of the mask with dq, dk, dv or the workspace.
+inline int validate_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                               const void* dO, const void* dq, const void* dk, const void* dv, const Shape& s,
+                               float scale, const void* ws, size_t ws_bytes) {
+  return validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, 0, ws, ws_bytes);
+}
+
+inline int validate_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                                    const void* dO, const void* dq, const void* dk, const void* dv, const Shape& s,
+                                    float scale, int causal, const void* block_mask, int per_head, const void* ws,
+                                    size_t ws_bytes) {
+  if (!block_mask) return kErrNull;
+  int st = validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, ws, ws_bytes);
+  if (st != kOk) return st;
+  if (s.N > kMaxBlockSparseN) return kErrShape;
+  if (per_head != 0 && per_head != 1) return kErrArg;
+  const size_t mb = block_mask_bytes(s, per_head);
+  const size_t tb = size_t(tensor_elems(s)) * 2;
+  const void* outs[4] = {dq, dk, dv, ws};
+  const size_t outsz[4] = {tb, tb, tb, bwd_workspace_bytes(s)};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(block_mask, mb, outs[i], outsz[i])) return kErrArg;
+  return kOk;
+}
+
 inline int check_dropout_p(float p) { return (std::isfinite(p) && p >= 0.0f && p < 1.0f) ? kOk : kErrArg; }
 
 inline const char* status_string(int st) {

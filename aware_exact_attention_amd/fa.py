@@ -43,6 +43,10 @@ SIGNATURES = {
                                 ctypes.c_ulonglong, _vp]),
     "fa_bwd_dropout": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
                                 _c_int, _c_float, ctypes.c_ulonglong, _vp, _c_size_t, _vp]),
+    "fa_bwd_window": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
+                               _c_int, _c_int, _vp, _c_size_t, _vp]),
+    "fa_bwd_blocksparse": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                    _c_float, _c_int, _vp, _c_int, _vp, _c_size_t, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -297,6 +301,60 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
     if st != 0:
         raise FAError(st, "fa_fwd_blocksparse")
     return out, lse
+
+
+def _bwd_args(q, k, v, o, lse, do, scale, workspace, out):
+    """Shared checks and allocations of the bf16 masked backward calls."""
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    _check(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", torch.uint8)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            _check(t, n, torch.bfloat16, (B, H, N, d))
+    return (B, H, N, d), float(scale), workspace, (dq, dk, dv)
+
+
+def bwd_window(q, k, v, o, lse, do, window_left: int, window_right: int, scale: float | None = None,
+               workspace=None, out=None):
+    """bf16 backward of ``fwd_window`` (``fa_bwd_window``); returns ``(dq, dk, dv)``."""
+    lib = load()
+    (B, H, N, d), scale, workspace, (dq, dk, dv) = _bwd_args(q, k, v, o, lse, do, scale, workspace, out)
+    st = lib.fa_bwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, int(window_left),
+                           int(window_right), workspace.data_ptr(), workspace.numel(), _stream())
+    if st != 0:
+        raise FAError(st, "fa_bwd_window")
+    return dq, dk, dv
+
+
+def bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal: bool = False, scale: float | None = None,
+                    workspace=None, out=None):
+    """bf16 backward of ``fwd_blocksparse`` (``fa_bwd_blocksparse``); returns ``(dq, dk, dv)``."""
+    lib = load()
+    (B, H, N, d), scale, workspace, (dq, dk, dv) = _bwd_args(q, k, v, o, lse, do, scale, workspace, out)
+    nb = (N + 63) // 64
+    if block_mask.dim() == 3:
+        _check(block_mask, "block_mask", torch.uint8, (H, nb, nb))
+        per_head = 1
+    else:
+        _check(block_mask, "block_mask", torch.uint8, (nb, nb))
+        per_head = 0
+    st = lib.fa_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale,
+                                int(bool(causal)), block_mask.data_ptr(), per_head, workspace.data_ptr(),
+                                workspace.numel(), _stream())
+    if st != 0:
+        raise FAError(st, "fa_bwd_blocksparse")
+    return dq, dk, dv
 
 
 def fwd_dropout(q, k, v, dropout_p: float, seed: int, causal: bool = False, scale: float | None = None,

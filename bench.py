@@ -242,10 +242,17 @@ def next_rows():
     pairs = sum(min(N - 1, i + 512) - max(0, i - 512) + 1 for i in range(N))
     t_w = _graph_ms(lambda: fa.fwd_window(q, k, v, 512, 512, out=o, lse=lse), 10)
     fl_w = 4 * B * H * pairs * d
+    dob = torch.randn(q.shape, generator=torch.Generator().manual_seed(10)).to(torch.bfloat16).cuda()
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    wsb = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    fa.fwd_window(q, k, v, 512, 512, out=o, lse=lse)
+    t_wb = _graph_ms(lambda: fa.bwd_window(q, k, v, o, lse, dob, 512, 512, workspace=wsb, out=grads), 10)
     res["window_512_512_B1H8N16384d128"] = {
         "ms": round(t_w, 5), "visible_fraction": round(pairs / N / N, 4), "dense_fa_fwd_ms": round(t_d, 5),
         "tflops_visible": round(fl_w / (t_w * 1e-3) / 1e12, 1),
-        "frac_peak": round(fl_w / (t_w * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        "frac_peak": round(fl_w / (t_w * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "bwd_ms": round(t_wb, 5), "bwd_tflops_visible": round(2.5 * fl_w / (t_wb * 1e-3) / 1e12, 1),
+        "bwd_frac_peak": round(2.5 * fl_w / (t_wb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     nb = N // 64
     g = torch.Generator().manual_seed(9)
     bm = (torch.rand((nb, nb), generator=g) < 0.5).to(torch.uint8)
@@ -253,10 +260,14 @@ def next_rows():
     bmd = bm.cuda()
     t_b = _graph_ms(lambda: fa.fwd_blocksparse(q, k, v, bmd, out=o, lse=lse), 5)
     fl_b = 4 * B * H * kept * 64 * 64 * d
+    fa.fwd_blocksparse(q, k, v, bmd, out=o, lse=lse)
+    t_bb = _graph_ms(lambda: fa.bwd_blocksparse(q, k, v, o, lse, dob, bmd, workspace=wsb, out=grads), 5)
     res["blocksparse_half_B1H8N16384d128"] = {
         "ms": round(t_b, 5), "kept_blocks": round(kept / nb / nb, 4), "dense_fa_fwd_ms": round(t_d, 5),
         "tflops_visible": round(fl_b / (t_b * 1e-3) / 1e12, 1),
-        "frac_peak": round(fl_b / (t_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        "frac_peak": round(fl_b / (t_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "bwd_ms": round(t_bb, 5), "bwd_tflops_visible": round(2.5 * fl_b / (t_bb * 1e-3) / 1e12, 1),
+        "bwd_frac_peak": round(2.5 * fl_b / (t_bb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     # fp16 inputs at the benchmark shape (fa_fwd_fp16, fa_bwd_fp16)
     q16, k16, v16, do16 = (t.cuda() for t in make_inputs(B, H, N, d, "fp16", 9, 1.0, backward=True))
     o16 = torch.empty_like(q16)
@@ -272,8 +283,6 @@ def next_rows():
         "bwd_frac_peak": round(2.5 * fl_f / (t_b16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "peak_note": "fp16 dense MFMA peak equals bf16's (2516.6 TFLOP/s)"}
     # dropout p = 0.1 at the benchmark shape (fa_fwd_dropout, fa_bwd_dropout)
-    grads = tuple(torch.empty_like(q) for _ in range(3))
-    dob = torch.randn(q.shape, generator=torch.Generator().manual_seed(10)).to(torch.bfloat16).cuda()
     t_fd = _graph_ms(lambda: fa.fwd_dropout(q, k, v, 0.1, 1234, out=o, lse=lse), 3)
     t_bd = _graph_ms(lambda: fa.bwd_dropout(q, k, v, o, lse, dob, 0.1, 1234, workspace=ws16, out=grads), 3)
     res["dropout_p0.1_B1H8N16384d128"] = {

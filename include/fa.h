@@ -250,6 +250,30 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int N, int d, float scale, int causal,
                        const unsigned char* block_mask, int mask_per_head, hipStream_t stream);
 
+/*
+ * fa_bwd_window, fa_bwd_blocksparse - bf16 backward of fa_fwd_window and
+ * fa_fwd_blocksparse: the gradients dq, dk, dv of sum(o * dO) for the same
+ * visible set, by the recomputation of fa_bwd (FlashAttention-from-GPU-memory
+ * page, section 2.2; FlashAttention optimisation page, section 4.2).  o and
+ * lse are exactly what the matching forward returned for the same window or
+ * mask (a row that saw no key: o = 0, lse = -inf; its dq row is 0 and it adds
+ * nothing to dk, dv).  Query steps and key tiles outside every visible block
+ * are skipped.  Parameters, layouts, workspace (fa_bwd_workspace_bytes) and
+ * ownership as fa_bwd; window_left / window_right as fa_fwd_window;
+ * causal, block_mask and mask_per_head as fa_fwd_blocksparse.
+ * Errors: as fa_bwd, plus (block-sparse) N <= 65536 (FA_ERR_SHAPE),
+ * mask_per_head in {0, 1} (FA_ERR_ARG), block_mask not NULL (FA_ERR_NULL) and
+ * not overlapping dq, dk, dv or the workspace (FA_ERR_ARG).
+ */
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                  int window_left, int window_right, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                       int causal, const unsigned char* block_mask, int mask_per_head, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
 /* fa_status_string - static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

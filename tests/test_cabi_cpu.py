@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
                                            "fa_fwd_fp16", "fa_bwd_fp16", "fa_fwd_dropout", "fa_bwd_dropout",
                                            "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_bytes",
                                            "fa_fwd_splitkv", "fa_lse_merge", "fa_fwd_window",
-                                           "fa_fwd_blocksparse", "fa_status_string"])
+                                           "fa_fwd_blocksparse", "fa_bwd_window", "fa_bwd_blocksparse",
+                                           "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -217,6 +218,24 @@ def test_mask_validation(lib):
     assert fb(q, k, v, o, l, B, H, N, d, 0.125, 2, m.ptr, 1, None) == ST["ARG"]
     assert fb(q, k, v, o, l, B, H, N, d, 0.125, 0, m.ptr, 2, None) == ST["ARG"]
     assert fb(q, k, v, o, l, B, H, N, d, 0.125, 0, o, 1, None) == ST["ARG"]      # mask overlaps the output
+    # masked backward: fa_bwd's checks plus the mask's
+    bb = [_Buf(B * H * N * d * 2) for _ in range(9)]
+    ptrs = [b.ptr for b in bb]
+    need = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    ws = _Buf(need)
+    gw = lib.fa_bwd_window
+    assert gw(None, *ptrs[1:], B, H, N, d, 0.125, 4, 4, ws.ptr, need, None) == ST["NULL"]
+    assert gw(*ptrs, B, H, N, 80, 0.125, 4, 4, ws.ptr, need, None) == ST["HEAD_DIM"]
+    assert gw(*ptrs, B, H, N, d, 0.125, 4, 4, None, 0, None) == ST["WORKSPACE"]
+    assert gw(*ptrs, B, H, N, d, 0.125, 4, 4, ws.ptr, need - 1, None) == ST["WORKSPACE"]
+    assert gw(*ptrs[:6], ptrs[0], *ptrs[7:], B, H, N, d, 0.125, 4, 4, ws.ptr, need, None) == ST["ARG"]  # dq over q
+    gb = lib.fa_bwd_blocksparse
+    assert gb(*ptrs, B, H, N, d, 0.125, 0, None, 1, ws.ptr, need, None) == ST["NULL"]
+    assert gb(*ptrs, B, H, 65537, d, 0.125, 0, m.ptr, 1, ws.ptr, need, None) in (ST["SHAPE"], ST["WORKSPACE"])
+    assert gb(*ptrs, B, H, N, d, 0.125, 2, m.ptr, 1, ws.ptr, need, None) == ST["ARG"]
+    assert gb(*ptrs, B, H, N, d, 0.125, 0, m.ptr, 2, ws.ptr, need, None) == ST["ARG"]
+    assert gb(*ptrs, B, H, N, d, 0.125, 0, ptrs[7], 1, ws.ptr, need, None) == ST["ARG"]  # mask overlaps dk
+    assert gb(*ptrs, B, H, N, d, 0.125, 0, m.ptr, 1, None, 0, None) == ST["WORKSPACE"]
 
 
 def test_dropout_validation(lib):
@@ -248,7 +267,7 @@ using namespace fa;
 static int fails = 0;
 #define EXPECT(x) do { if (!(x)) { std::printf("FAIL line %d: %s\n", __LINE__, #x); ++fails; } } while (0)
 int main() {
-  alignas(16) static char mem[9][8192];
+  alignas(16) static char mem[10][8192];
   alignas(16) static char ws[1 << 16];
   Shape s{1, 2, 16, 64};
   EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 0, 2) == kOk);
@@ -296,6 +315,16 @@ int main() {
   EXPECT(validate_fwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 1, nullptr, 1) == kErrNull);
   EXPECT(validate_fwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f, 1, mem[3], 1) == kErrArg);
   EXPECT(validate_fwd_window(mem[0], mem[1], mem[2], mem[3], mem[4], s, 0.125f) == kOk);
+  EXPECT(validate_bwd_window(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s, 0.125f,
+                             ws, sizeof ws) == kOk);
+  EXPECT(validate_bwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s,
+                                  0.125f, 1, mem[9], 1, ws, sizeof ws) == kOk);
+  EXPECT(validate_bwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s,
+                                  0.125f, 1, nullptr, 1, ws, sizeof ws) == kErrNull);
+  EXPECT(validate_bwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s,
+                                  0.125f, 1, mem[6], 1, ws, sizeof ws) == kErrArg);
+  EXPECT(validate_bwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s,
+                                  0.125f, 1, mem[9], 3, ws, sizeof ws) == kErrArg);
   EXPECT(check_dropout_p(0.0f) == kOk && check_dropout_p(0.999f) == kOk);
   EXPECT(check_dropout_p(1.0f) == kErrArg && check_dropout_p(-1e-9f) == kErrArg && check_dropout_p(NAN) == kErrArg);
   return fails ? 1 : 0;
