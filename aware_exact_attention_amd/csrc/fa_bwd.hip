@@ -40,7 +40,7 @@
 
 namespace fa {
 
-// Byte offset, inside a row-major tile with rows of 2*DD bytes swizzled by
+// Byte offset, inside a row-major LDS tile (rows of lds_row_bytes<DD>()) swizzled by
 // tile_swz<DD>, of the 8 bytes this lane reads with ds_read_b64_tr_b16 so that
 // lane l ends up with column 32*b + l%32 of rows row0 + {4h+8r2+0..3}
 // (h = l/32): in its 16-lane group g (lane t) it addresses row
@@ -50,7 +50,7 @@ __device__ __forceinline__ int tr_off(int b, int r2, int lane) {
   const int g = lane >> 4, t = lane & 15;
   const int row = 4 * (g >> 1) + 8 * r2 + (t >> 2);
   const int col = 32 * b + 16 * (g & 1) + 4 * (t & 3);
-  return row * (2 * DD) + (((col >> 3) ^ tile_swz<DD>(row)) * 16) + (col & 7) * 2;
+  return row * lds_row_bytes<DD>() + (((col >> 3) ^ tile_swz<DD>(row)) * 16) + (col & 7) * 2;
 }
 
 template <typename E>
@@ -69,15 +69,7 @@ __device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, i
 #endif
 }
 
-// Source byte offset of the 16 bytes that a direct load places at byte p of a
-// row-major tile with rows of 2*DD bytes: LDS unit (row, pu) holds logical
-// unit pu ^ tile_swz<DD>(row) of that row.
-template <int DD>
-__device__ __forceinline__ int swz_src(int p) {
-  constexpr int RS = 2 * DD;
-  const int row = p / RS, pu = (p % RS) / 16;
-  return row * RS + ((pu ^ tile_swz<DD>(row)) * 16);
-}
+
 
 // ---------------------------------------------------------------------------
 // 1. D = rowsum(dO * O) and LSE2 = LSE * log2(e) (+inf for LSE = -inf).  8 lanes per row.
@@ -86,8 +78,10 @@ template <typename E, int D>
 __global__ void __launch_bounds__(256)
 bwd_pre_kernel(const E* __restrict__ O, const E* __restrict__ dO, const float* __restrict__ LSE,
                float* __restrict__ Dv, float* __restrict__ lse2, long long rows) {
-  using v8 = typename Vec<E>::v8;
+  // vectors of 8 elements (4 when d / 8 is not a multiple of 8: d = 96)
   constexpr int PER = D / 8;  // elements per lane
+  constexpr int VW = PER % 8 == 0 ? 8 : 4;
+  typedef E vec_t __attribute__((ext_vector_type(VW)));
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gid >> 3;
   const int sub = threadIdx.x & 7;
@@ -96,11 +90,11 @@ bwd_pre_kernel(const E* __restrict__ O, const E* __restrict__ dO, const float* _
     const E* o = O + row * D + sub * PER;
     const E* g = dO + row * D + sub * PER;
 #pragma unroll
-    for (int u = 0; u < PER / 8; ++u) {
-      const v8 a = *reinterpret_cast<const v8*>(o + 8 * u);
-      const v8 b = *reinterpret_cast<const v8*>(g + 8 * u);
+    for (int u = 0; u < PER / VW; ++u) {
+      const vec_t a = *reinterpret_cast<const vec_t*>(o + VW * u);
+      const vec_t b = *reinterpret_cast<const vec_t*>(g + VW * u);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+      for (int e = 0; e < VW; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
     }
   }
   acc += __shfl_xor(acc, 1);
@@ -142,7 +136,8 @@ struct DkdvTile {
   static constexpr int KS = D / 16;            // 16-wide k steps over d
   static constexpr int DB = D / 32;            // 32-column blocks over d
   static constexpr int PS = BQ / 16;           // 16-query k steps of dV, dK
-  static constexpr int RS = D * 2;             // bytes per Q / dO row
+  static constexpr int RS = lds_row_bytes<D>(); // bytes per Q / dO row in LDS
+  static constexpr int GRS = D * 2;            // bytes per Q / dO / K / V row in HBM
   static constexpr int QT = BQ * RS;           // bytes of one Q or dO tile
   static constexpr int OFF_DO = QT;
   static constexpr int OFF_LSE = 2 * QT;       // BQ floats of LSE*log2(e)
@@ -156,7 +151,7 @@ struct DkdvTile {
   static constexpr int M = D / 8;
   static constexpr int H = M / 2;
   static constexpr int PF = 3;                 // operand reads in flight
-  static constexpr int PP = 8 / H;             // element pairs of VALU work per slot
+  static constexpr int PP = (8 + H - 1) / H;   // element pairs of VALU work per slot (8 pairs per block)
   // first slots of: P of block 0, dS of block 0, P of block 1, dS of block 1
   static constexpr int P0 = H + 2, D0 = 2 * H + 1, P1 = 3 * H + 2, D1 = 4 * H + 1;
 };
@@ -187,7 +182,7 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
   const int jt = tile - bh * Tk;  // causal: key block 0 has the most query steps and is dispatched first
   const int k0 = jt * T::BKV;
   const size_t head = size_t(bh) * N * D;
-  const int head_bytes = N * T::RS;
+  const int head_bytes = N * T::GRS;
 
   // K and V fragments of this wave's keys (lane: key k0 + 32*wave + l32,
   // d = 16*st + 8*half .. +7).  Keys past N read as zero; their dK and dV
@@ -199,8 +194,8 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head, head_bytes);
 #pragma unroll
     for (int st = 0; st < T::KS; ++st) {
-      kf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rk, key * T::RS + (16 * st + 8 * half) * 2, 0, 0));
-      vf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rv, key * T::RS + (16 * st + 8 * half) * 2, 0, 0));
+      kf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rk, key * T::GRS + (16 * st + 8 * half) * 2, 0, 0));
+      vf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rv, key * T::GRS + (16 * st + 8 * half) * 2, 0, 0));
     }
     // Kept in AGPRs for the whole sweep: the MFMAs take them from there, and
     // the VGPRs are left to the accumulators and the per-step values.
@@ -220,7 +215,7 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
   const float* dh = Dv + size_t(bh) * N;
   auto issue_loads = [&](int i, int stage) {
     const int q0 = i * T::BQ;
-    const int bytes = (N - q0) * T::RS;
+    const int bytes = (N - q0) * T::GRS;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head + size_t(q0) * D, bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(dO + head + size_t(q0) * D, bytes);
     char* dst = smem + stage * T::STAGE + wave * T::LPW * 1024;
@@ -401,10 +396,13 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
         constexpr int t = decltype(tc)::value;
         using Z = std::integral_constant<int, 0>;
         using O = std::integral_constant<int, 1>;
-        if constexpr (u >= T::P0 && u < T::P0 + H) p_pair(Z{}, std::integral_constant<int, 2 * (T::PP * (u - T::P0) + t)>{});
-        if constexpr (u >= T::D0 && u < T::D0 + H) ds_pair(Z{}, std::integral_constant<int, 2 * (T::PP * (u - T::D0) + t)>{});
-        if constexpr (u >= T::P1 && u < T::P1 + H) p_pair(O{}, std::integral_constant<int, 2 * (T::PP * (u - T::P1) + t)>{});
-        if constexpr (u >= T::D1 && u < T::D1 + H) ds_pair(O{}, std::integral_constant<int, 2 * (T::PP * (u - T::D1) + t)>{});
+        // pair index within the block's 8 pairs (past 7: nothing, when H*PP > 8)
+        constexpr int jp0 = T::PP * (u - T::P0) + t, jd0 = T::PP * (u - T::D0) + t;
+        constexpr int jp1 = T::PP * (u - T::P1) + t, jd1 = T::PP * (u - T::D1) + t;
+        if constexpr (u >= T::P0 && u < T::P0 + H && jp0 < 8) p_pair(Z{}, std::integral_constant<int, 2 * jp0>{});
+        if constexpr (u >= T::D0 && u < T::D0 + H && jd0 < 8) ds_pair(Z{}, std::integral_constant<int, 2 * jd0>{});
+        if constexpr (u >= T::P1 && u < T::P1 + H && jp1 < 8) p_pair(O{}, std::integral_constant<int, 2 * jp1>{});
+        if constexpr (u >= T::D1 && u < T::D1 + H && jd1 < 8) ds_pair(O{}, std::integral_constant<int, 2 * jd1>{});
       });
       // keep the slot order: the scheduler would otherwise pull each LDS read
       // next to its MFMA and bunch the VALU work
@@ -429,10 +427,10 @@ bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
       u32x2 w;
       w[0] = pack2<E>(accv[b][4 * g + 0] * fv, accv[b][4 * g + 1] * fv);
       w[1] = pack2<E>(accv[b][4 * g + 2] * fv, accv[b][4 * g + 3] * fv);
-      __builtin_amdgcn_raw_buffer_store_b64(w, rvo, key * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, rvo, key * T::GRS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
       w[0] = pack2<E>(acck[b][4 * g + 0] * scale, acck[b][4 * g + 1] * scale);
       w[1] = pack2<E>(acck[b][4 * g + 2] * scale, acck[b][4 * g + 3] * scale);
-      __builtin_amdgcn_raw_buffer_store_b64(w, rko, key * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, rko, key * T::GRS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
 }
 
@@ -449,7 +447,8 @@ struct DqTile {
   static constexpr int DB = D / 32;               // 32-column blocks of dQ
   static constexpr int KB = BC / 32;              // 32-key blocks of S^T
   static constexpr int PS = BC / 16;              // 16-key k steps of dQ^T
-  static constexpr int RS = D * 2;                // bytes per K or V row
+  static constexpr int RS = lds_row_bytes<D>();   // bytes per K or V row in LDS
+  static constexpr int GRS = D * 2;               // bytes per row in HBM
   static constexpr int TILE = BC * RS;            // bytes of one K or V tile
   static constexpr int STAGE = 2 * TILE;          // K tile then V tile
   static constexpr int LPW = TILE / 1024 / NW;
@@ -490,7 +489,7 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
   const size_t head = size_t(bh) * N * D;
   const E* Kh = K + head;
   const E* Vh = V + head;
-  const int head_bytes = N * T::RS;
+  const int head_bytes = N * T::GRS;
 
   // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): row
   // qrow, columns 16*s + 8*half .. +7.  Rows past N read as zero.
@@ -502,7 +501,7 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(dO + head, head_bytes);
 #pragma unroll
     for (int s = 0; s < T::KS; ++s) {
-      const int off = qrow * T::RS + (16 * s + 8 * half) * 2;
+      const int off = qrow * T::GRS + (16 * s + 8 * half) * 2;
       qf[s] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
       df[s] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
     }
@@ -564,7 +563,7 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
   for (int u = 0; u < T::LPW; ++u) goff[u] = swz_src<D>((wave * T::LPW + u) * 1024 + 16 * lane);
   auto issue_loads = [&](int j, int stage) {
     const int key0 = j * T::BC;
-    const int bytes = (N - key0) * T::RS;
+    const int bytes = (N - key0) * T::GRS;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + size_t(key0) * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + size_t(key0) * D, bytes);
     char* dst = smem + stage * T::STAGE + wave * T::LPW * 1024;
@@ -725,7 +724,7 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
       u32x2 w;
       w[0] = pack2<E>(acc[b][4 * g + 0] * scale, acc[b][4 * g + 1] * scale);
       w[1] = pack2<E>(acc[b][4 * g + 2] * scale, acc[b][4 * g + 3] * scale);
-      __builtin_amdgcn_raw_buffer_store_b64(w, ro, qrow * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, qrow * T::GRS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
 }
 
@@ -780,6 +779,9 @@ template <typename E>
 static hipError_t launch_bwd_e(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                                int causal, void* ws, hipStream_t st) {
+  if (d == 96)
+    return causal ? launch_bwd_t<E, 96, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st)
+                  : launch_bwd_t<E, 96, false>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st);
   if (d == 128)
     return causal ? launch_bwd_t<E, 128, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st)
                   : launch_bwd_t<E, 128, false>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st);
@@ -797,6 +799,9 @@ hipError_t launch_bwd_dropout(const void* q, const void* k, const void* v, const
                               const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                               int causal, float p, unsigned long long seed, void* ws, hipStream_t st) {
   const DropArgs dp = make_drop_args(p, seed);
+  if (d == 96)
+    return causal ? launch_bwd_t<__bf16, 96, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
+                  : launch_bwd_t<__bf16, 96, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
   if (d == 128)
     return causal ? launch_bwd_t<__bf16, 128, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
                   : launch_bwd_t<__bf16, 128, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
@@ -843,6 +848,8 @@ hipError_t launch_bwd_window(const void* q, const void* k, const void* v, const 
                              int left, int right, void* ws, hipStream_t st) {
   // a bound of N - 1 or more limits nothing: the same as no bound
   const MaskArgs mk{left >= N - 1 ? -1 : left, right >= N - 1 ? -1 : right, nullptr, 0, 0, H};
+  if (d == 96)
+    return launch_bwd_masked_t<96, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
   if (d == 128)
     return launch_bwd_masked_t<128, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
   return launch_bwd_masked_t<64, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
@@ -854,6 +861,11 @@ hipError_t launch_bwd_blocksparse(const void* q, const void* k, const void* v, c
                                   hipStream_t st) {
   const int nb = (N + kMaskBlock - 1) / kMaskBlock;
   const MaskArgs mk{-1, -1, bm, per_head ? (long long)nb * nb : 0, nb, H};
+  if (d == 96)
+    return causal ? launch_bwd_masked_t<96, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                                 ws, st)
+                  : launch_bwd_masked_t<96, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                                  ws, st);
   if (d == 128)
     return causal ? launch_bwd_masked_t<128, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
                                                                  ws, st)

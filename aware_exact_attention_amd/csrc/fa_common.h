@@ -78,8 +78,16 @@ __device__ __forceinline__ int swz(int row, int unit) {
   else return unit ^ ((row ^ (row >> 3)) & 7);
 }
 
+// Bytes of one row of a K, V, Q or dO tile in LDS.  Rows in HBM are 2*D
+// bytes; at d = 96 the LDS rows are padded to 256 bytes (12 of their 16
+// units hold data) so that d = 128's swizzle applies unchanged.
+template <int D>
+constexpr int lds_row_bytes() {
+  return D == 96 ? 256 : 2 * D;
+}
+
 // Swizzle of the 16-byte units of one row of a row-major K or V tile in LDS
-// (d = 128: 16 units per 256-byte row; d = 64: 8 units per 128-byte row).
+// (d = 128 and 96: 16 units per 256-byte row; d = 64: 8 units per 128-byte row).
 // Physical unit = logical unit ^ tile_swz<D>(row).  The tables were chosen so
 // that both access patterns of the tiles hit distinct banks, whether the LDS
 // serves 16 lanes x 16 bytes or 8 lanes x 16 bytes per cycle:
@@ -88,7 +96,7 @@ __device__ __forceinline__ int swz(int row, int unit) {
 template <int D>
 __device__ __forceinline__ int tile_swz(int row) {
   const int r = row & 15;
-  if constexpr (D == 128) {
+  if constexpr (D == 128 || D == 96) {
     const int i = r & 3;  // {0, 6, 10, 12}[i] ^ (r / 4)
     const int p = ((i >> 1) << 3) | ((i & 1) << 2) | (((i ^ (i >> 1)) & 1) << 1);
     return p ^ (r >> 2);
@@ -113,6 +121,19 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, 
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voffset, 0, 0, 0);
 #endif
+}
+
+// Source byte offset, within HBM rows of 2*D bytes, of the 16 bytes that a
+// direct load places at byte p of a row-major LDS tile (rows of
+// lds_row_bytes<D>()): LDS unit (row, pu) holds logical unit
+// pu ^ tile_swz<D>(row) of that row.  Padding units (d = 96) get an offset
+// past every buffer, so their loads read zeros and touch no memory.
+template <int D>
+__device__ __forceinline__ int swz_src(int p) {
+  constexpr int LRS = lds_row_bytes<D>();
+  const int row = p / LRS, pu = (p % LRS) / 16;
+  const int lu = pu ^ tile_swz<D>(row);
+  return lu < D / 8 ? row * (2 * D) + lu * 16 : 0x7fffff00;
 }
 
 // Pack two fp32 values into two bf16 (round to nearest even) in one dword.

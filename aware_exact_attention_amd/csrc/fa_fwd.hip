@@ -46,7 +46,8 @@ struct FwdTile {
   static constexpr int DB = D / 32;               // 32-column blocks of O
   static constexpr int KB = BC / 32;              // 32-key blocks of S
   static constexpr int PS = BC / 16;              // 16-key k steps of P V
-  static constexpr int RS = D * 2;                // bytes per tile row (K and V alike)
+  static constexpr int RS = lds_row_bytes<D>();   // bytes per tile row in LDS (K and V alike)
+  static constexpr int GRS = D * 2;               // bytes per row in HBM
   static constexpr int TILE = BC * RS;            // bytes of one K or V tile
   static constexpr int STAGE = 2 * TILE;          // K tile then V tile
   static constexpr int LPW = TILE / 1024 / NW;    // 1 KiB direct-to-LDS loads per wave per tile
@@ -104,7 +105,7 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   const size_t head = size_t(bh) * N * D;
   const E* Kh = K + head;
   const E* Vh = V + head;
-  const int head_bytes = N * T::RS;
+  const int head_bytes = N * T::GRS;
 
   // Q fragment (B operand of S^T = K Q^T): row qrow, columns 16*s + 8*half .. +7.
   // Rows past N read as zero (buffer bounds).
@@ -116,7 +117,7 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
 #pragma unroll
     for (int s = 0; s < T::KS; ++s)
       qf[s] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(
-                                             rq, qrow * T::RS + (16 * s + 8 * half) * 2, 0, 0));
+                                             rq, qrow * T::GRS + (16 * s + 8 * half) * 2, 0, 0));
   }
 
   const int Tc = (N + T::BC - 1) / T::BC;
@@ -176,14 +177,10 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   // belong at byte 16*l of that range under the swizzle.
   int goff[T::LPW];
 #pragma unroll
-  for (int i = 0; i < T::LPW; ++i) {
-    const int p = (wave * T::LPW + i) * 1024 + 16 * lane;
-    const int row = p / T::RS, pu = (p % T::RS) / 16;
-    goff[i] = row * T::RS + ((pu ^ tile_swz<D>(row)) * 16);
-  }
+  for (int i = 0; i < T::LPW; ++i) goff[i] = swz_src<D>((wave * T::LPW + i) * 1024 + 16 * lane);
   auto issue_loads = [&](int j, int stage) {
     const int key0 = j * T::BC;
-    const int bytes = (N - key0) * T::RS;
+    const int bytes = (N - key0) * T::GRS;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + size_t(key0) * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + size_t(key0) * D, bytes);
     char* kdst = smem + stage * T::STAGE + wave * T::LPW * 1024;
@@ -396,7 +393,7 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
       u32x2 w;
       w[0] = pack2<E>(o[b][4 * g + 0] * inv, o[b][4 * g + 1] * inv);
       w[1] = pack2<E>(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
-      __builtin_amdgcn_raw_buffer_store_b64(w, ro, qrow * T::RS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, qrow * T::GRS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
     }
   if (half == 0 && qrow < N) LSE[size_t(bh) * N + qrow] = (!BLOCKS || lt > 0.f) ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
 }
@@ -529,6 +526,8 @@ static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void
 template <typename E>
 static hipError_t launch_fwd_e(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                int N, int d, float scale, int causal, hipStream_t st) {
+  if (d == 96) return causal ? launch_fwd_t<E, 96, true>(q, k, v, o, lse, B, H, N, scale, st)
+                              : launch_fwd_t<E, 96, false>(q, k, v, o, lse, B, H, N, scale, st);
   if (d == 128) return causal ? launch_fwd_t<E, 128, true>(q, k, v, o, lse, B, H, N, scale, st)
                               : launch_fwd_t<E, 128, false>(q, k, v, o, lse, B, H, N, scale, st);
   return causal ? launch_fwd_t<E, 64, true>(q, k, v, o, lse, B, H, N, scale, st)
@@ -560,6 +559,8 @@ hipError_t launch_fwd_dropout(const void* q, const void* k, const void* v, void*
                               int N, int d, float scale, int causal, float p, unsigned long long seed,
                               hipStream_t st) {
   const DropArgs dp = make_drop_args(p, seed);
+  if (d == 96) return causal ? launch_fwd_dropout_t<96, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
+                              : launch_fwd_dropout_t<96, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
   if (d == 128) return causal ? launch_fwd_dropout_t<128, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
                               : launch_fwd_dropout_t<128, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
   return causal ? launch_fwd_dropout_t<64, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
@@ -635,7 +636,10 @@ hipError_t launch_lse_merge(const float* op, const float* lp, int S, void* o, fl
   const long long threads = rows * (d / 8);
   const long long blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (d == 128)
+  if (d == 96)
+    hipLaunchKernelGGL((lse_merge_kernel<96>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
+                       lse, rows);
+  else if (d == 128)
     hipLaunchKernelGGL((lse_merge_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
                        lse, rows);
   else
@@ -669,6 +673,8 @@ static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v
 
 hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                               int N, int d, float scale, int causal, int S, void* ws, hipStream_t st) {
+  if (d == 96) return causal ? launch_fwd_split_t<96, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
+                              : launch_fwd_split_t<96, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
   if (d == 128) return causal ? launch_fwd_split_t<128, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
                               : launch_fwd_split_t<128, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
   return causal ? launch_fwd_split_t<64, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
@@ -694,6 +700,7 @@ hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* 
                              int d, float scale, int left, int right, hipStream_t st) {
   // a bound of N - 1 or more limits nothing: the same as no bound
   const MaskArgs mk{left >= N - 1 ? -1 : left, right >= N - 1 ? -1 : right, nullptr, 0, 0, H};
+  if (d == 96) return launch_fwd_masked_t<96, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
   if (d == 128) return launch_fwd_masked_t<128, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
   return launch_fwd_masked_t<64, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
 }
@@ -703,6 +710,9 @@ hipError_t launch_fwd_blocksparse(const void* q, const void* k, const void* v, v
                                   hipStream_t st) {
   const int nb = (N + kMaskBlock - 1) / kMaskBlock;
   const MaskArgs mk{-1, -1, bm, per_head ? (long long)nb * nb : 0, nb, H};
+  if (d == 96)
+    return causal ? launch_fwd_masked_t<96, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
+                  : launch_fwd_masked_t<96, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
   if (d == 128)
     return causal ? launch_fwd_masked_t<128, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
                   : launch_fwd_masked_t<128, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
@@ -723,6 +733,8 @@ static hipError_t launch_fwd_f32_t(const float* q, const float* k, const float* 
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int B, int H, int N, int d, float scale, int causal, hipStream_t st) {
+  if (d == 96) return causal ? launch_fwd_f32_t<96, true>(q, k, v, o, lse, B, H, N, scale, st)
+                              : launch_fwd_f32_t<96, false>(q, k, v, o, lse, B, H, N, scale, st);
   if (d == 128) return causal ? launch_fwd_f32_t<128, true>(q, k, v, o, lse, B, H, N, scale, st)
                               : launch_fwd_f32_t<128, false>(q, k, v, o, lse, B, H, N, scale, st);
   return causal ? launch_fwd_f32_t<64, true>(q, k, v, o, lse, B, H, N, scale, st)

@@ -282,6 +282,20 @@ def next_rows():
         "bwd_ms": round(t_b16, 5), "bwd_tflops": round(2.5 * fl_f / (t_b16 * 1e-3) / 1e12, 1),
         "bwd_frac_peak": round(2.5 * fl_f / (t_b16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "peak_note": "fp16 dense MFMA peak equals bf16's (2516.6 TFLOP/s)"}
+    # head dimension 96 (LDS rows padded to 256 bytes) at B1 H8 N16384, bf16
+    q96, k96, v96, do96 = (t.cuda() for t in make_inputs(B, H, N, 96, "bf16", 9, 1.0, backward=True))
+    o96 = torch.empty_like(q96)
+    g96 = tuple(torch.empty_like(q96) for _ in range(3))
+    ws96 = torch.empty(fa.bwd_workspace_bytes(B, H, N, 96), dtype=torch.uint8, device="cuda")
+    t_f96 = _graph_ms(lambda: fa.fwd(q96, k96, v96, out=o96, lse=lse), 3)
+    t_b96 = _graph_ms(lambda: fa.bwd(q96, k96, v96, o96, lse, do96, workspace=ws96, out=g96), 3)
+    fl_96 = 4 * B * H * N * N * 96
+    res["d96_B1H8N16384"] = {
+        "fwd_ms": round(t_f96, 5), "fwd_tflops": round(fl_96 / (t_f96 * 1e-3) / 1e12, 1),
+        "fwd_frac_peak": round(fl_96 / (t_f96 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "bwd_ms": round(t_b96, 5), "bwd_tflops": round(2.5 * fl_96 / (t_b96 * 1e-3) / 1e12, 1),
+        "bwd_frac_peak": round(2.5 * fl_96 / (t_b96 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q96, k96, v96, do96, o96, g96, ws96
     # dropout p = 0.1 at the benchmark shape (fa_fwd_dropout, fa_bwd_dropout)
     t_fd = _graph_ms(lambda: fa.fwd_dropout(q, k, v, 0.1, 1234, out=o, lse=lse), 3)
     t_bd = _graph_ms(lambda: fa.bwd_dropout(q, k, v, o, lse, dob, 0.1, 1234, workspace=ws16, out=grads), 3)

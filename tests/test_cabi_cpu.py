@@ -90,7 +90,7 @@ def test_fwd_validation(lib, fn):
     assert f(q, k, v, o, l, 1, 1, 0, 64, 0.125, 0, None) == ST["SHAPE"]
     assert f(q, k, v, o, l, 1 << 12, 1 << 10, 1 << 10, 64, 0.125, 0, None) == ST["SHAPE"]
     assert f(q, k, v, o, l, 1, 1, (1 << 22) - 256, 128, 0.125, 0, None) == ST["SHAPE"]  # one head > 2^31 B fp32
-    assert f(q, k, v, o, l, 1, 1, 8, 96, 0.125, 0, None) == ST["HEAD_DIM"]
+    assert f(q, k, v, o, l, 1, 1, 8, 80, 0.125, 0, None) == ST["HEAD_DIM"]
     assert f(q, k, v, o, l, 1, 1, 8, 256, 0.125, 0, None) == ST["HEAD_DIM"]
     assert f(q, k, v, o, l, 1, 1, 8, 64, float("nan"), 0, None) == ST["SCALE"]
     assert f(q, k, v, o, l, 1, 1, 8, 64, float("inf"), 0, None) == ST["SCALE"]
@@ -158,7 +158,7 @@ def test_splitkv_parts_and_workspace(lib):
     assert parts(1, 1, 640, 64, 100) == 10
     assert parts(1, 1, 576, 64, 4) == 3         # 9 tiles, 3 per part
     assert parts(1, 1, 1 << 20, 64, 1000) == 64
-    assert parts(0, 1, 64, 64, 2) == 0 and parts(1, 1, 64, 96, 2) == 0
+    assert parts(0, 1, 64, 64, 2) == 0 and parts(1, 1, 64, 80, 2) == 0
     ws = lib.fa_fwd_splitkv_workspace_bytes
     rows = 8 * 2048
     assert ws(1, 8, 2048, 128, 0) == 4 * rows * 128 * 4 + 4 * rows * 4
@@ -176,7 +176,7 @@ def test_splitkv_validation(lib):
     wsb = _Buf(need)
     f = lib.fa_fwd_splitkv
     assert f(None, k, v, o, l, B, H, N, d, 0.125, 0, 2, wsb.ptr, need, None) == ST["NULL"]
-    assert f(q, k, v, o, l, B, H, N, 96, 0.125, 0, 2, wsb.ptr, need, None) == ST["HEAD_DIM"]
+    assert f(q, k, v, o, l, B, H, N, 80, 0.125, 0, 2, wsb.ptr, need, None) == ST["HEAD_DIM"]
     assert f(q, k, v, o, l, B, H, N, d, 0.0, 0, 2, wsb.ptr, need, None) == ST["SCALE"]
     assert f(q, k, v, o, l, B, H, N, d, 0.125, 3, 2, wsb.ptr, need, None) == ST["ARG"]
     assert f(q, k, v, o, l, B, H, N, d, 0.125, 0, 2, None, 0, None) == ST["WORKSPACE"]
@@ -245,7 +245,7 @@ def test_dropout_validation(lib):
     assert f(q, k, v, o, l, 1, 1, 8, 64, 0.125, 0, -0.1, 7, None) == ST["ARG"]
     assert f(q, k, v, o, l, 1, 1, 8, 64, 0.125, 0, 1.0, 7, None) == ST["ARG"]
     assert f(q, k, v, o, l, 1, 1, 8, 64, 0.125, 0, float("nan"), 7, None) == ST["ARG"]
-    assert f(q, k, v, o, l, 1, 1, 8, 96, 0.125, 0, 0.1, 7, None) == ST["HEAD_DIM"]
+    assert f(q, k, v, o, l, 1, 1, 8, 80, 0.125, 0, 0.1, 7, None) == ST["HEAD_DIM"]
     B, H, N, d = 1, 2, 16, 64
     bb = [_Buf(B * H * N * d * 2) for _ in range(9)]
     ptrs = [b.ptr for b in bb]

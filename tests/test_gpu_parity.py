@@ -114,7 +114,7 @@ def test_tiny_f32(gpu_lib):
 
 
 @pytest.mark.parametrize("N", [1, 3, 31, 100, 129, 1000, 4097])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_bf16(gpu_lib, N, d, causal):
     q, k, v = make_inputs(1, 2, N, d, "bf16", seed=100 + N)
@@ -126,7 +126,7 @@ def test_ragged_bf16(gpu_lib, N, d, causal):
 
 
 @pytest.mark.parametrize("N", [1, 5, 63, 65, 300])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_f32(gpu_lib, N, d, causal):
     q, k, v = make_inputs(2, 1, N, d, "f32", seed=200 + N)
@@ -157,7 +157,7 @@ def test_gpt2_shape(gpu_lib, name):
 
 
 @pytest.mark.parametrize("N", [300, 1000])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_bf16_many_heads(gpu_lib, N, d, causal):
     """Many heads of a ragged length: large grids, both head dims, both masks,
@@ -220,7 +220,7 @@ def _bwd_case(fa, q, k, v, do, causal, scale):
 
 
 @pytest.mark.parametrize("N", [1, 33, 130, 300, 1000])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_small(gpu_lib, N, d, causal):
     q, k, v, do = make_inputs(1, 2, N, d, "bf16", seed=400 + N, backward=True)
