@@ -750,12 +750,12 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
 
   const int Tk = (N + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV;
   const long long Gk = (long long)B * H * Tk;
-  // dQ pass: eight waves (256 rows) per workgroup for d = 128 grids that cover
+  // dQ pass: eight waves (256 rows) per workgroup for d = 128 and 96 grids that cover
   // every CU (each K/V tile streamed once for twice the rows); four waves
   // otherwise.  Unlike the forward, the causal dQ pass gains from eight waves
   // too (1-2 % at B4 H16 N4096 and B2 H8 N16000).
   const long long Gq8 = (long long)B * H * ((N + DqTile<D, 8>::BR - 1) / DqTile<D, 8>::BR);
-  const bool dq8 = D == 128 && Gq8 >= kNumCUs;
+  const bool dq8 = (D == 128 || D == 96) && Gq8 >= kNumCUs;
   const int Tr = dq8 ? (N + DqTile<D, 8>::BR - 1) / DqTile<D, 8>::BR : (N + DqTile<D, 4>::BR - 1) / DqTile<D, 4>::BR;
   const long long Gq = (long long)B * H * Tr;
   if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
