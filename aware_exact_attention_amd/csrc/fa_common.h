@@ -87,7 +87,9 @@ constexpr int lds_row_bytes() {
 }
 
 // Swizzle of the 16-byte units of one row of a row-major K or V tile in LDS
-// (d = 128 and 96: 16 units per 256-byte row; d = 64: 8 units per 128-byte row).
+// (d = 128 and 96: 16 units per 256-byte row; d = 64: 8 units per 128-byte
+// row; d = 256: 32 units per 512-byte row, d = 128's table on the low four
+// bits of the unit).
 // Physical unit = logical unit ^ tile_swz<D>(row).  The tables were chosen so
 // that both access patterns of the tiles hit distinct banks, whether the LDS
 // serves 16 lanes x 16 bytes or 8 lanes x 16 bytes per cycle:
@@ -96,7 +98,9 @@ constexpr int lds_row_bytes() {
 template <int D>
 __device__ __forceinline__ int tile_swz(int row) {
   const int r = row & 15;
-  if constexpr (D == 128 || D == 96) {
+  if constexpr (D == 256) {
+    return tile_swz<128>(row);
+  } else if constexpr (D == 128 || D == 96) {
     const int i = r & 3;  // {0, 6, 10, 12}[i] ^ (r / 4)
     const int p = ((i >> 1) << 3) | ((i & 1) << 2) | (((i ^ (i >> 1)) & 1) << 1);
     return p ^ (r >> 2);

@@ -68,7 +68,7 @@ struct SplitArgs {
 
 
 template <typename E, int D, bool CAUSAL, int NW, bool SPLIT, int MODE, bool DROP>
-__global__ void __launch_bounds__(64 * NW, 8 / NW)
+__global__ void __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW)
 fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V, E* __restrict__ O,
            float* __restrict__ LSE, int N, int Tr, float c, SplitArgs sp, MaskArgs mk, DropArgs dp) {
   using T = FwdTile<D, NW>;
@@ -519,7 +519,8 @@ template <typename E, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                int N, float scale, hipStream_t st) {
   const long long G8 = (long long)B * H * ((N + FwdTile<D, 8>::BR - 1) / FwdTile<D, 8>::BR);
-  if ((D == 128 || D == 96) && !CAUSAL && G8 >= kNumCUs) return launch_fwd_nw<E, D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, st);
+  if constexpr (D == 128 || D == 96)
+    if (!CAUSAL && G8 >= kNumCUs) return launch_fwd_nw<E, D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, st);
   return launch_fwd_nw<E, D, CAUSAL, 4>(q, k, v, o, lse, B, H, N, scale, st);
 }
 
@@ -528,6 +529,8 @@ static hipError_t launch_fwd_e(const void* q, const void* k, const void* v, void
                                int N, int d, float scale, int causal, hipStream_t st) {
   if (d == 96) return causal ? launch_fwd_t<E, 96, true>(q, k, v, o, lse, B, H, N, scale, st)
                               : launch_fwd_t<E, 96, false>(q, k, v, o, lse, B, H, N, scale, st);
+  if (d == 256) return causal ? launch_fwd_t<E, 256, true>(q, k, v, o, lse, B, H, N, scale, st)
+                              : launch_fwd_t<E, 256, false>(q, k, v, o, lse, B, H, N, scale, st);
   if (d == 128) return causal ? launch_fwd_t<E, 128, true>(q, k, v, o, lse, B, H, N, scale, st)
                               : launch_fwd_t<E, 128, false>(q, k, v, o, lse, B, H, N, scale, st);
   return causal ? launch_fwd_t<E, 64, true>(q, k, v, o, lse, B, H, N, scale, st)
@@ -550,8 +553,8 @@ template <int D, bool CAUSAL>
 static hipError_t launch_fwd_dropout_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                        int H, int N, float scale, const DropArgs& dp, hipStream_t st) {
   const long long G8 = (long long)B * H * ((N + FwdTile<D, 8>::BR - 1) / FwdTile<D, 8>::BR);
-  if (D == 128 && !CAUSAL && G8 >= kNumCUs)
-    return launch_fwd_nw<__bf16, D, CAUSAL, 8, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
+  if constexpr (D == 128)
+    if (!CAUSAL && G8 >= kNumCUs) return launch_fwd_nw<__bf16, D, CAUSAL, 8, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
   return launch_fwd_nw<__bf16, D, CAUSAL, 4, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
 }
 
@@ -561,6 +564,8 @@ hipError_t launch_fwd_dropout(const void* q, const void* k, const void* v, void*
   const DropArgs dp = make_drop_args(p, seed);
   if (d == 96) return causal ? launch_fwd_dropout_t<96, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
                               : launch_fwd_dropout_t<96, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
+  if (d == 256) return causal ? launch_fwd_dropout_t<256, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
+                              : launch_fwd_dropout_t<256, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
   if (d == 128) return causal ? launch_fwd_dropout_t<128, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
                               : launch_fwd_dropout_t<128, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
   return causal ? launch_fwd_dropout_t<64, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
@@ -636,7 +641,10 @@ hipError_t launch_lse_merge(const float* op, const float* lp, int S, void* o, fl
   const long long threads = rows * (d / 8);
   const long long blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (d == 96)
+  if (d == 256)
+    hipLaunchKernelGGL((lse_merge_kernel<256>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
+                       lse, rows);
+  else if (d == 96)
     hipLaunchKernelGGL((lse_merge_kernel<96>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
                        lse, rows);
   else if (d == 128)
@@ -675,6 +683,8 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               int N, int d, float scale, int causal, int S, void* ws, hipStream_t st) {
   if (d == 96) return causal ? launch_fwd_split_t<96, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
                               : launch_fwd_split_t<96, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
+  if (d == 256) return causal ? launch_fwd_split_t<256, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
+                              : launch_fwd_split_t<256, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
   if (d == 128) return causal ? launch_fwd_split_t<128, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
                               : launch_fwd_split_t<128, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
   return causal ? launch_fwd_split_t<64, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
@@ -701,6 +711,7 @@ hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* 
   // a bound of N - 1 or more limits nothing: the same as no bound
   const MaskArgs mk{left >= N - 1 ? -1 : left, right >= N - 1 ? -1 : right, nullptr, 0, 0, H};
   if (d == 96) return launch_fwd_masked_t<96, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  if (d == 256) return launch_fwd_masked_t<256, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
   if (d == 128) return launch_fwd_masked_t<128, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
   return launch_fwd_masked_t<64, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
 }
@@ -713,6 +724,9 @@ hipError_t launch_fwd_blocksparse(const void* q, const void* k, const void* v, v
   if (d == 96)
     return causal ? launch_fwd_masked_t<96, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
                   : launch_fwd_masked_t<96, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  if (d == 256)
+    return causal ? launch_fwd_masked_t<256, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
+                  : launch_fwd_masked_t<256, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
   if (d == 128)
     return causal ? launch_fwd_masked_t<128, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
                   : launch_fwd_masked_t<128, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
@@ -735,6 +749,8 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           int B, int H, int N, int d, float scale, int causal, hipStream_t st) {
   if (d == 96) return causal ? launch_fwd_f32_t<96, true>(q, k, v, o, lse, B, H, N, scale, st)
                               : launch_fwd_f32_t<96, false>(q, k, v, o, lse, B, H, N, scale, st);
+  if (d == 256) return causal ? launch_fwd_f32_t<256, true>(q, k, v, o, lse, B, H, N, scale, st)
+                              : launch_fwd_f32_t<256, false>(q, k, v, o, lse, B, H, N, scale, st);
   if (d == 128) return causal ? launch_fwd_f32_t<128, true>(q, k, v, o, lse, B, H, N, scale, st)
                               : launch_fwd_f32_t<128, false>(q, k, v, o, lse, B, H, N, scale, st);
   return causal ? launch_fwd_f32_t<64, true>(q, k, v, o, lse, B, H, N, scale, st)

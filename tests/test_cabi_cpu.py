@@ -91,7 +91,7 @@ def test_fwd_validation(lib, fn):
     assert f(q, k, v, o, l, 1 << 12, 1 << 10, 1 << 10, 64, 0.125, 0, None) == ST["SHAPE"]
     assert f(q, k, v, o, l, 1, 1, (1 << 22) - 256, 128, 0.125, 0, None) == ST["SHAPE"]  # one head > 2^31 B fp32
     assert f(q, k, v, o, l, 1, 1, 8, 80, 0.125, 0, None) == ST["HEAD_DIM"]
-    assert f(q, k, v, o, l, 1, 1, 8, 256, 0.125, 0, None) == ST["HEAD_DIM"]
+    assert f(q, k, v, o, l, 1, 1, 8, 512, 0.125, 0, None) == ST["HEAD_DIM"]
     assert f(q, k, v, o, l, 1, 1, 8, 64, float("nan"), 0, None) == ST["SCALE"]
     assert f(q, k, v, o, l, 1, 1, 8, 64, float("inf"), 0, None) == ST["SCALE"]
     assert f(q, k, v, o, l, 1, 1, 8, 64, 0.0, 0, None) == ST["SCALE"]
@@ -133,6 +133,7 @@ def test_bwd_validation(lib, fn):
     assert call(dk=None) == ST["NULL"]
     assert call(N=0) == ST["SHAPE"]
     assert call(d=32) == ST["HEAD_DIM"]
+    assert call(d=256) == ST["HEAD_DIM"]  # d = 256: forward entry points only
     assert call(scale=float("nan")) == ST["SCALE"]
     assert call(causal=-1) == ST["ARG"]
     assert call(ws=None) == ST["WORKSPACE"]
@@ -325,6 +326,13 @@ int main() {
                                   0.125f, 1, mem[6], 1, ws, sizeof ws) == kErrArg);
   EXPECT(validate_bwd_blocksparse(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s,
                                   0.125f, 1, mem[9], 3, ws, sizeof ws) == kErrArg);
+  EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], Shape{1, 1, 8, 256}, 0.125f, 0, 2) == kOk);
+  EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], Shape{1, 1, 8, 96}, 0.125f, 0, 2) == kOk);
+  EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], Shape{1, 1, 8, 256},
+                      0.125f, 1, ws, sizeof ws) == kErrHeadDim);
+  EXPECT(bwd_workspace_bytes(Shape{1, 1, 8, 256}) == 0 && bwd_workspace_bytes(Shape{1, 1, 8, 96}) > 0);
+  EXPECT(split_count(Shape{1, 1, 256, 256}, 2) == 2);
+  EXPECT(validate_lse_merge(mem[0], mem[1], 2, mem[2], mem[3], Shape{1, 1, 8, 256}) == kOk);
   EXPECT(check_dropout_p(0.0f) == kOk && check_dropout_p(0.999f) == kOk);
   EXPECT(check_dropout_p(1.0f) == kErrArg && check_dropout_p(-1e-9f) == kErrArg && check_dropout_p(NAN) == kErrArg);
   return fails ? 1 : 0;

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("N", [1, 100, 1000, 4097])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp16_forward(gpu_lib, N, d, causal):
     q, k, v = make_inputs(1, 2, N, d, "fp16", seed=1000 + N + d)

@@ -29,7 +29,7 @@ def _nan_outputs(q):
 
 
 @pytest.mark.parametrize("N", [1, 100, 1000, 3000])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("window", WINDOWS, ids=[f"{a}_{b}" for a, b in WINDOWS])
 def test_window_small(gpu_lib, N, d, window):
     left, right = window
@@ -68,7 +68,7 @@ def _check_blocksparse(tag, o, lse, ro, rl):
 
 
 @pytest.mark.parametrize("N", [64, 130, 1000, 2049])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("per_head", [False, True])
 def test_blocksparse_small(gpu_lib, N, d, causal, per_head):

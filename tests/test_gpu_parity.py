@@ -114,7 +114,7 @@ def test_tiny_f32(gpu_lib):
 
 
 @pytest.mark.parametrize("N", [1, 3, 31, 100, 129, 1000, 4097])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_bf16(gpu_lib, N, d, causal):
     q, k, v = make_inputs(1, 2, N, d, "bf16", seed=100 + N)
@@ -126,7 +126,7 @@ def test_ragged_bf16(gpu_lib, N, d, causal):
 
 
 @pytest.mark.parametrize("N", [1, 5, 63, 65, 300])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_f32(gpu_lib, N, d, causal):
     q, k, v = make_inputs(2, 1, N, d, "f32", seed=200 + N)

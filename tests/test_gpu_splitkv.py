@@ -36,7 +36,7 @@ def _splitkv(fa, q, k, v, causal, scale, num_splits):
 
 
 @pytest.mark.parametrize("N", [1, 100, 1000, 4097])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("splits", [0, 3, 7])
 def test_splitkv_small(gpu_lib, N, d, causal, splits):
@@ -95,7 +95,7 @@ def test_splitkv_benchmark_shape_matches_fwd(gpu_lib):
 
 
 @pytest.mark.parametrize("S", [1, 2, 5])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 def test_lse_merge(gpu_lib, S, d):
     B, H, N = 1, 3, 77
     rng = np.random.default_rng(700 + S + d)
