@@ -137,6 +137,30 @@ def ref_bwd(q, k, v, do, scale: float, causal: bool):
     return dq, dk, dv
 
 
+def ref_bwd_rows(q, k, v, do, scale: float, causal: bool, rows, keys):
+    """One head ``[N,d]``: dQ of the query rows ``rows``, and what those rows add to dK and dV at the keys ``keys``.
+
+    Every gradient term of a query row depends on that row alone (its P row,
+    its dP row and its D_i), so ``dQ[rows]`` is ``ref_bwd``'s dQ restricted to
+    the rows, and dK, dV are sums over the rows of per-row terms.  When the
+    rows include every row that sees a key, the sums at that key are complete:
+    the last T keys of a causal head are seen by the last T rows only.  Used on
+    workloads too large to materialise in full.  Returns float64
+    ``(dQ[rows], dK part [len(keys), d], dV part [len(keys), d])``.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    qr, dor = _as_f64(np.asarray(q)[rows], np.asarray(do)[rows])
+    k, v = _as_f64(k, v)
+    s = scale * (qr @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > rows[:, None], -np.inf, s)
+    p = _softmax_rows(s)[0]
+    dp = dor @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return scale * (ds @ k), scale * (ds[:, keys].T @ qr), p[:, keys].T @ dor
+
+
 def ref_bwd_delta(o, do):
     """``D_i = sum_k dO_ik * O_ik`` per row, ``[B,H,N]`` (equals ``sum_j P_ij dP_ij``)."""
     o, do = _as_f64(o, do)

@@ -199,6 +199,30 @@ def pin_autograd(R):
         np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-13)
 
 
+def pin_bwd_rows(R):
+    """The row-subset backward against torch autograd (fp64, CPU) of sum(O * dO) with dO
+    zeroed outside the rows: dQ of the rows, and the rows' whole contribution to dK, dV."""
+    B, H, N, d = 1, 1, 23, 6
+    arrs = [_rand((B, H, N, d), 70 + i, 1.5) for i in range(4)]
+    scale = 0.35
+    cases = [([0, 3, 22, 11], [0, 5, 22], False), ([2, 19, 20, 21, 22], [19, 20, 21, 22], True),
+             (list(range(N)), list(range(N)), True)]
+    for rows, keys, causal in cases:
+        tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in arrs[:3])
+        s = scale * (tq @ tk.transpose(-1, -2))
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+        o = torch.softmax(s, -1) @ tv
+        dmask = np.zeros_like(arrs[3])
+        dmask[0, 0, rows] = arrs[3][0, 0, rows]
+        (o * torch.from_numpy(dmask)).sum().backward()
+        dq, dk, dv = R.ref_bwd_rows(arrs[0][0, 0], arrs[1][0, 0], arrs[2][0, 0], arrs[3][0, 0], scale, causal,
+                                    rows, keys)
+        np.testing.assert_allclose(dq, tq.grad.numpy()[0, 0, rows], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dk, tk.grad.numpy()[0, 0, keys], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dv, tv.grad.numpy()[0, 0, keys], rtol=0, atol=1e-13)
+
+
 def pin_gradient_invariants(R):
     B, H, N, d = 1, 2, 19, 8
     q, k, v, do = (_rand((B, H, N, d), 70 + i) for i in range(4))
@@ -230,7 +254,7 @@ def pin_large_spread(R):
 
 PINS = [pin_golden, pin_rows_sum_to_one, pin_constant_keys, pin_dominant_score,
         pin_causal_row0_and_n1, pin_shift_and_permutation, pin_tiled_equals_direct,
-        pin_torch_sdpa, pin_finite_differences, pin_autograd, pin_gradient_invariants,
+        pin_torch_sdpa, pin_finite_differences, pin_autograd, pin_bwd_rows, pin_gradient_invariants,
         pin_large_spread]
 
 
