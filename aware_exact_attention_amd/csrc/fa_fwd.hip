@@ -31,9 +31,17 @@
 
 namespace fa {
 
-// Largest lead (log2 units) of a tile's row max over the running reference
-// before the reference moves; bounds P by 2^8 = 256.
+// When the reference of a row moves, it moves to the row max unless that
+// leads the old reference by at most this much (log2 units).
 constexpr float kLazyRescale = 8.f;
+// The reference moves only on a tile where a lane's sum of P over its 32
+// elements reaches kSumBound (so some P >= 2^35), or while the row has none.
+// Until then every P < 2^40: with at most 2^22 keys and |V| < 2^8, O and l
+// stay below 2^70, far from fp32 overflow, and no precision is lost (a
+// floating-point P keeps its relative precision at any scale).  Rows whose
+// scores keep climbing (large-spread scores) therefore rarely take the
+// rescale path, which every row of the wave then pays for.
+constexpr float kSumBound = 1099511627776.f;  // 2^40
 
 
 template <int D, int NW_>
@@ -267,33 +275,18 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
         }
     }
     // ---- online softmax (scale > 0, so max(score)*c == max(score*c)).
-    // The reference m of a row moves only when a tile's row max exceeds it by
-    // more than kLazyRescale (log2 units), so P <= 2^kLazyRescale and the O
-    // and l rescale is skipped on most tiles; softmax is invariant to the
-    // reference.  Each lane tests its own half of the row; only when some
-    // lane of the wave needs a new reference are the halves combined and
-    // the reference, O and l updated.
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    if (__builtin_amdgcn_ballot_w64(mx * c > m + kLazyRescale)) {
-      const float mxr = halves_max(mx) * c;
-      const float m_new = (mxr > m + kLazyRescale) ? mxr : m;
-      const float mu_new = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet in this row
-      const float alpha = exp2_fast(mu - mu_new);  // O and l are still 0 while m is -inf
-      m = m_new;
-      mu = mu_new;
-      l *= alpha;
-#pragma unroll
-      for (int b = 0; b < T::DB; ++b) o[b] *= alpha;
-    }
-    // P, rounded to the input type for the PV product; l sums the fp32 values
-    // (before dropout: the statistic is that of the softmax itself).  With
-    // dropout, bit kb*16 + r of `keep` says whether element (kb, r) survives:
-    // registers 4m .. 4m+3 of a key block hold 4 consecutive keys of this row,
-    // one Philox block row.
+    // P = exp2(S*c - mu) is taken against the row's current reference first.
+    // The reference m moves (and O, l are rescaled) only on a tile where this
+    // lane's half-row sum reaches kSumBound, or while the row has no reference
+    // yet (m = -inf, no key seen).  Otherwise every P stays below kSumBound;
+    // softmax is invariant to the reference.  The row max is taken only on
+    // those rare tiles, and their exponentials are taken again against the
+    // new reference.
+    // P is rounded to the input type for the PV product; l sums the fp32
+    // values (before dropout: the statistic is that of the softmax itself).
+    // With dropout, bit kb*16 + r of `keep` says whether element (kb, r)
+    // survives: registers 4m .. 4m+3 of a key block hold 4 consecutive keys of
+    // this row, one Philox block row.
     unsigned keep = 0;
     if constexpr (DROP) {
 #pragma unroll
@@ -305,17 +298,38 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
         }
     }
     v8 pb[T::PS];
-    float rs = 0.f;
+    float rs;
+    auto exps = [&]() {
+      rs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
+      for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s[kb][r], c, -mu));
-        rs += p;
-        float pd = p;  // dropout: the kept P; the 1/(1-p) scale is applied to O at the end
-        if constexpr (DROP) pd = ((keep >> (kb * 16 + r)) & 1u) ? p : 0.f;
-        pb[kb * 2 + (r >> 3)][r & 7] = (E)pd;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(fmaf(s[kb][r], c, -mu));
+          rs += p;
+          float pd = p;  // dropout: the kept P; the 1/(1-p) scale is applied to O at the end
+          if constexpr (DROP) pd = ((keep >> (kb * 16 + r)) & 1u) ? p : 0.f;
+          pb[kb * 2 + (r >> 3)][r & 7] = (E)pd;
+        }
+    };
+    exps();
+    if (__builtin_amdgcn_ballot_w64(m == -INFINITY || !(rs < kSumBound))) {
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      const float mxr = halves_max(mx) * c;
+      const float m_new = (mxr > m + kLazyRescale) ? mxr : m;
+      const float mu_new = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet in this row
+      const float alpha = exp2_fast(mu - mu_new);  // O and l are still 0 while m is -inf
+      m = m_new;
+      mu = mu_new;
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < T::DB; ++b) o[b] *= alpha;
+      exps();
+    }
     l += rs;
     // ---- O^T += V_j^T P^T: DB independent chains; V^T operands come from two
     // transposing reads of the row-major V tile, VPF operands ahead

@@ -146,6 +146,40 @@ def test_other_scale_and_peaked_rows(gpu_lib):
     check_lse("scale0.3_peaked", _np(lse), rl)
 
 
+@pytest.mark.parametrize("slope", [0.05, 0.3, 0.7, -0.4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_climbing_scores(gpu_lib, slope, causal):
+    """Scores that change steadily along the keys (scale*q.k_j = slope * j / ln 2
+    in log2 units, plus small noise), so the running maximum of a row moves on
+    every tile (slope 0.7: about 65 log2 units per 64-key tile), lags it by tens
+    of log2 units for several tiles (0.3, 0.05), or never moves after the first
+    tile (negative slope).  The forward against the oracle, and dV of the
+    backward (which takes P from the forward's LSE).  dQ and dK are not compared
+    here: with a key component as large as 0.05 * j they sum dS terms about ten
+    times larger than the result, so the bf16 rounding of dS (2^-9 relative)
+    alone exceeds the relative tolerance.  That is the conditioning of these
+    inputs, not of the method; the other backward tests cover dQ and dK."""
+    N, d = 1000, 64
+    q, k, v, do = make_inputs(1, 2, N, d, "bf16", seed=310, backward=True)
+    q = q * 0.05
+    q[..., 0] = 1.0
+    k = k * 0.05
+    k[..., 0] = (torch.arange(N, dtype=torch.float32) * slope).to(torch.bfloat16)
+    scale = 1.0
+    qd, kd, vd, dod = _gpu(q, k, v, do)
+    o, lse = gpu_lib.fwd(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = gpu_lib.bwd(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    args = [to_f64(t) for t in (q, k, v, do)]
+    ro, rl = oracle.ref_fwd(*args[:3], scale, causal)
+    _, _, rv = oracle.ref_bwd(*args, scale, causal)
+    tag = f"climbing slope={slope} causal={causal}"
+    check_o(tag, _np(o), ro)
+    check_lse(tag, _np(lse), rl)
+    check_grad(tag, "dV", _np(dv), rv)
+    assert torch.isfinite(dq).all().item() and torch.isfinite(dk).all().item()
+
+
 @pytest.mark.parametrize("name", ["gpt2", "gpt2_causal"])
 def test_gpt2_shape(gpu_lib, name):
     w = WORKLOADS[name]
