@@ -1,7 +1,8 @@
 """Build libfa.so (gfx950 only) in-tree with hipcc.
 
 Usage: ``python -m aware_exact_attention_amd.build`` (or ``build()`` from Python).
-Every call recompiles.  The library lands next to this file as ``libfa.so``.
+Every call recompiles (the three sources in parallel, objects under ``_build/``).
+The library lands next to this file as ``libfa.so``.
 """
 from __future__ import annotations
 
@@ -34,15 +35,35 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile each source to an object in parallel, then link libfa.so."""
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f for f in FLAGS if f != "-shared"] + list(extra_flags or [])
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [HIPCC, *flags, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    objs, failed = [], []
+    for src, obj, pr in procs:
+        out, _ = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(src)
+        objs.append(obj)
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-I", os.path.join(HERE, "..", "include"), *srcs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -19,28 +19,28 @@ hipError_t launch_bwd_fp16(const void* q, const void* k, const void* v, const vo
                            int causal, void* ws, hipStream_t st);
 hipError_t launch_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                               int N, int d, float scale, int causal, float p, unsigned long long seed,
-                              hipStream_t st);
+                              bool fp16, hipStream_t st);
 hipError_t launch_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
                               const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-                              int causal, float p, unsigned long long seed, void* ws, hipStream_t st);
+                              int causal, float p, unsigned long long seed, void* ws, bool fp16, hipStream_t st);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                           int N, int d, float scale, int causal, hipStream_t st);
 hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                              int N, int d, float scale, int causal, int S, void* ws, hipStream_t st);
+                              int N, int d, float scale, int causal, int S, void* ws, bool fp16, hipStream_t st);
 hipError_t launch_lse_merge(const float* op, const float* lp, int S, void* o, float* lse, int B, int H, int N,
-                            int d, hipStream_t st);
+                            int d, bool fp16, hipStream_t st);
 hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-                             int d, float scale, int left, int right, hipStream_t st);
+                             int d, float scale, int left, int right, bool fp16, hipStream_t st);
 hipError_t launch_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                   int N, int d, float scale, int causal, const unsigned char* bm, int per_head,
-                                  hipStream_t st);
+                                  bool fp16, hipStream_t st);
 hipError_t launch_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
                              const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-                             int left, int right, void* ws, hipStream_t st);
+                             int left, int right, void* ws, bool fp16, hipStream_t st);
 hipError_t launch_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                                   float scale, int causal, const unsigned char* bm, int per_head, void* ws,
-                                  hipStream_t st);
+                                  bool fp16, hipStream_t st);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                       int causal, void* ws, hipStream_t st);
@@ -70,8 +70,8 @@ int check_device() {
 
 extern "C" {
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-           float scale, int causal, hipStream_t stream) {
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, float scale,
+           int causal, hipStream_t stream) {
   const fa::Shape s{B, H, N, d};
   int st = fa::validate_fwd(q, k, v, o, lse, s, scale, causal, 2);
   if (st != fa::kOk) return st;
@@ -117,23 +117,34 @@ int fa_bwd_fp16(const void* q, const void* k, const void* v, const void* o, cons
              : fa::kErrHip;
 }
 
-int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                   float scale, int causal, float dropout_p, unsigned long long seed, hipStream_t stream) {
+static int fa_fwd_dropout_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                               int d, float scale, int causal, float dropout_p, unsigned long long seed,
+                               hipStream_t stream, bool fp16) {
   const fa::Shape s{B, H, N, d};
   int st = fa::validate_fwd(q, k, v, o, lse, s, scale, causal, 2);
   if (st == fa::kOk) st = fa::check_dropout_p(dropout_p);
   if (st != fa::kOk) return st;
   st = fa::check_device();
   if (st != fa::kOk) return st;
-  return fa::launch_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed, stream) == hipSuccess
+  return fa::launch_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed, fp16, stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
 }
 
-int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
-                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                   float dropout_p, unsigned long long seed, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, float dropout_p, unsigned long long seed, hipStream_t stream) {
+  return fa_fwd_dropout_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed, stream, false);
+}
+
+int fa_fwd_dropout_fp16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                        float scale, int causal, float dropout_p, unsigned long long seed, hipStream_t stream) {
+  return fa_fwd_dropout_impl(q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed, stream, true);
+}
+
+static int fa_bwd_dropout_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                               int causal, float dropout_p, unsigned long long seed, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream, bool fp16) {
   const fa::Shape s{B, H, N, d};
   int st = fa::validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, workspace, workspace_bytes);
   if (st == fa::kOk) st = fa::check_dropout_p(dropout_p);
@@ -141,9 +152,24 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   st = fa::check_device();
   if (st != fa::kOk) return st;
   return fa::launch_bwd_dropout(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, dropout_p, seed,
-                                workspace, stream) == hipSuccess
+                                workspace, fp16, stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, float dropout_p,
+                   unsigned long long seed, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fa_bwd_dropout_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, dropout_p, seed, workspace,
+                             workspace_bytes, stream, false);
+}
+
+int fa_bwd_dropout_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                        void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                        float dropout_p, unsigned long long seed, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return fa_bwd_dropout_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, dropout_p, seed, workspace,
+                             workspace_bytes, stream, true);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) { return fa::bwd_workspace_bytes(fa::Shape{B, H, N, d}); }
@@ -170,55 +196,117 @@ int fa_fwd_splitkv_parts(int B, int H, int N, int d, int num_splits) {
   return fa::split_count(fa::Shape{B, H, N, d}, num_splits);
 }
 
-int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-                   float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+static int fa_fwd_splitkv_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                               int d, float scale, int causal, int num_splits, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream, bool fp16) {
   const fa::Shape s{B, H, N, d};
   int st = fa::validate_fwd_splitkv(q, k, v, o, lse, s, scale, causal, num_splits, workspace, workspace_bytes);
   if (st != fa::kOk) return st;
   st = fa::check_device();
   if (st != fa::kOk) return st;
   const int S = fa::split_count(s, num_splits);
-  return fa::launch_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, S, workspace, stream) == hipSuccess
+  return fa::launch_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, S, workspace, fp16, stream) == hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  return fa_fwd_splitkv_impl(q, k, v, o, lse, B, H, N, d, scale, causal, num_splits, workspace, workspace_bytes,
+                             stream, false);
+}
+
+int fa_fwd_splitkv_fp16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                        float scale, int causal, int num_splits, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return fa_fwd_splitkv_impl(q, k, v, o, lse, B, H, N, d, scale, causal, num_splits, workspace, workspace_bytes,
+                             stream, true);
+}
+
+static int fa_lse_merge_impl(const float* o_parts, const float* lse_parts, int num_parts, void* o, float* lse, int B,
+                             int H, int N, int d, hipStream_t stream, bool fp16) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_lse_merge(o_parts, lse_parts, num_parts, o, lse, s);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_lse_merge(o_parts, lse_parts, num_parts, o, lse, B, H, N, d, fp16, stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
 }
 
 int fa_lse_merge(const float* o_parts, const float* lse_parts, int num_parts, void* o, float* lse, int B, int H,
                  int N, int d, hipStream_t stream) {
+  return fa_lse_merge_impl(o_parts, lse_parts, num_parts, o, lse, B, H, N, d, stream, false);
+}
+
+int fa_lse_merge_fp16(const float* o_parts, const float* lse_parts, int num_parts, void* o, float* lse, int B, int H,
+                      int N, int d, hipStream_t stream) {
+  return fa_lse_merge_impl(o_parts, lse_parts, num_parts, o, lse, B, H, N, d, stream, true);
+}
+
+static int fa_fwd_window_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                              int d, float scale, int window_left, int window_right, hipStream_t stream, bool fp16) {
   const fa::Shape s{B, H, N, d};
-  int st = fa::validate_lse_merge(o_parts, lse_parts, num_parts, o, lse, s);
+  int st = fa::validate_fwd_window(q, k, v, o, lse, s, scale);
   if (st != fa::kOk) return st;
   st = fa::check_device();
   if (st != fa::kOk) return st;
-  return fa::launch_lse_merge(o_parts, lse_parts, num_parts, o, lse, B, H, N, d, stream) == hipSuccess
+  return fa::launch_fwd_window(q, k, v, o, lse, B, H, N, d, scale, window_left, window_right, fp16, stream) ==
+                 hipSuccess
              ? fa::kOk
              : fa::kErrHip;
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                   float scale, int window_left, int window_right, hipStream_t stream) {
-  const fa::Shape s{B, H, N, d};
-  int st = fa::validate_fwd_window(q, k, v, o, lse, s, scale);
-  if (st != fa::kOk) return st;
-  st = fa::check_device();
-  if (st != fa::kOk) return st;
-  return fa::launch_fwd_window(q, k, v, o, lse, B, H, N, d, scale, window_left, window_right, stream) ==
-                 hipSuccess
-             ? fa::kOk
-             : fa::kErrHip;
+  return fa_fwd_window_impl(q, k, v, o, lse, B, H, N, d, scale, window_left, window_right, stream, false);
 }
 
-int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-                       int d, float scale, int causal, const unsigned char* block_mask, int mask_per_head,
-                       hipStream_t stream) {
+int fa_fwd_window_fp16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                       float scale, int window_left, int window_right, hipStream_t stream) {
+  return fa_fwd_window_impl(q, k, v, o, lse, B, H, N, d, scale, window_left, window_right, stream, true);
+}
+
+static int fa_fwd_blocksparse_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                   int N, int d, float scale, int causal, const unsigned char* block_mask,
+                                   int mask_per_head, hipStream_t stream, bool fp16) {
   const fa::Shape s{B, H, N, d};
   int st = fa::validate_fwd_blocksparse(q, k, v, o, lse, s, scale, causal, block_mask, mask_per_head);
   if (st != fa::kOk) return st;
   st = fa::check_device();
   if (st != fa::kOk) return st;
-  return fa::launch_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, mask_per_head,
+  return fa::launch_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, mask_per_head, fp16,
                                     stream) == hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                       float scale, int causal, const unsigned char* block_mask, int mask_per_head, hipStream_t stream
+                       ) {
+  return fa_fwd_blocksparse_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, mask_per_head, stream,
+                                 false);
+}
+
+int fa_fwd_blocksparse_fp16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                            int d, float scale, int causal, const unsigned char* block_mask, int mask_per_head,
+                            hipStream_t stream) {
+  return fa_fwd_blocksparse_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, mask_per_head, stream, true);
+}
+
+static int fa_bwd_window_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                              int window_left, int window_right, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, bool fp16) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, s, scale, workspace, workspace_bytes);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, window_left, window_right,
+                               workspace, fp16, stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
 }
@@ -226,21 +314,21 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
 int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int window_left,
                   int window_right, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const fa::Shape s{B, H, N, d};
-  int st = fa::validate_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, s, scale, workspace, workspace_bytes);
-  if (st != fa::kOk) return st;
-  st = fa::check_device();
-  if (st != fa::kOk) return st;
-  return fa::launch_bwd_window(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, window_left, window_right,
-                               workspace, stream) == hipSuccess
-             ? fa::kOk
-             : fa::kErrHip;
+  return fa_bwd_window_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, window_left, window_right, workspace,
+                            workspace_bytes, stream, false);
 }
 
-int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-                       int causal, const unsigned char* block_mask, int mask_per_head, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+int fa_bwd_window_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                       void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int window_left,
+                       int window_right, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fa_bwd_window_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, window_left, window_right, workspace,
+                            workspace_bytes, stream, true);
+}
+
+static int fa_bwd_blocksparse_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                                   float scale, int causal, const unsigned char* block_mask, int mask_per_head,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream, bool fp16) {
   const fa::Shape s{B, H, N, d};
   int st = fa::validate_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, block_mask,
                                         mask_per_head, workspace, workspace_bytes);
@@ -248,9 +336,25 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
   st = fa::check_device();
   if (st != fa::kOk) return st;
   return fa::launch_bwd_blocksparse(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, block_mask,
-                                    mask_per_head, workspace, stream) == hipSuccess
+                                    mask_per_head, workspace, fp16, stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
+}
+
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                       void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                       const unsigned char* block_mask, int mask_per_head, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return fa_bwd_blocksparse_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, block_mask,
+                                 mask_per_head, workspace, workspace_bytes, stream, false);
+}
+
+int fa_bwd_blocksparse_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                            int causal, const unsigned char* block_mask, int mask_per_head, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return fa_bwd_blocksparse_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, block_mask,
+                                 mask_per_head, workspace, workspace_bytes, stream, true);
 }
 
 const char* fa_status_string(int status) { return fa::status_string(status); }

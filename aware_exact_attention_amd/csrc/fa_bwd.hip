@@ -795,28 +795,38 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
   return launch_bwd_e<__bf16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, ws, st);
 }
 
-hipError_t launch_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                              const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-                              int causal, float p, unsigned long long seed, void* ws, hipStream_t st) {
+template <typename E>
+static hipError_t launch_bwd_dropout_e(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                        const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                                        float scale, int causal, float p, unsigned long long seed, void* ws,
+                                        hipStream_t st) {
   const DropArgs dp = make_drop_args(p, seed);
   if (d == 96)
-    return causal ? launch_bwd_t<__bf16, 96, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
-                  : launch_bwd_t<__bf16, 96, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
+    return causal ? launch_bwd_t<E, 96, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
+                  : launch_bwd_t<E, 96, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
   if (d == 128)
-    return causal ? launch_bwd_t<__bf16, 128, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
-                  : launch_bwd_t<__bf16, 128, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
-  return causal ? launch_bwd_t<__bf16, 64, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
-                : launch_bwd_t<__bf16, 64, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
+    return causal ? launch_bwd_t<E, 128, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
+                  : launch_bwd_t<E, 128, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
+  return causal ? launch_bwd_t<E, 64, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
+                : launch_bwd_t<E, 64, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
 }
 
-// Sliding-window and block-sparse backward (bf16): the dense passes with a
+hipError_t launch_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                              int causal, float p, unsigned long long seed, void* ws, bool fp16, hipStream_t st) {
+  return fp16 ? launch_bwd_dropout_e<_Float16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, p, seed,
+                                                ws, st)
+              : launch_bwd_dropout_e<__bf16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, p, seed, ws,
+                                             st);
+}
+
+// Sliding-window and block-sparse backward: the dense passes with a
 // per-step predicate in the dK/dV pass and a per-tile one in the dQ pass
 // (four-wave workgroups: 128 queries, two 64-row mask blocks).
-template <int D, bool CAUSAL, int MODE>
+template <typename E, int D, bool CAUSAL, int MODE>
 static hipError_t launch_bwd_masked_t(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
                                       const MaskArgs& mk, void* ws, hipStream_t st) {
-  using E = __bf16;
   const long long rows = (long long)B * H * N;
   const BwdWorkspace w = bwd_workspace_layout(Shape{B, H, N, D});
   char* base = reinterpret_cast<char*>(ws);
@@ -843,38 +853,57 @@ static hipError_t launch_bwd_masked_t(const void* q, const void* k, const void* 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                             const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-                             int left, int right, void* ws, hipStream_t st) {
+template <typename E>
+static hipError_t launch_bwd_window_e(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                      const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                                      float scale, int left, int right, void* ws, hipStream_t st) {
   // a bound of N - 1 or more limits nothing: the same as no bound
   const MaskArgs mk{left >= N - 1 ? -1 : left, right >= N - 1 ? -1 : right, nullptr, 0, 0, H};
   if (d == 96)
-    return launch_bwd_masked_t<96, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
+    return launch_bwd_masked_t<E, 96, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
   if (d == 128)
-    return launch_bwd_masked_t<128, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
-  return launch_bwd_masked_t<64, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
+    return launch_bwd_masked_t<E, 128, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
+  return launch_bwd_masked_t<E, 64, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
+}
+
+template <typename E>
+static hipError_t launch_bwd_blocksparse_e(const void* q, const void* k, const void* v, const void* o,
+                                           const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
+                                           int H, int N, int d, float scale, int causal, const unsigned char* bm,
+                                           int per_head, void* ws, hipStream_t st) {
+  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+  const MaskArgs mk{-1, -1, bm, per_head ? (long long)nb * nb : 0, nb, H};
+  if (d == 96)
+    return causal ? launch_bwd_masked_t<E, 96, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                                 ws, st)
+                  : launch_bwd_masked_t<E, 96, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                                  ws, st);
+  if (d == 128)
+    return causal ? launch_bwd_masked_t<E, 128, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                                 ws, st)
+                  : launch_bwd_masked_t<E, 128, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                                  ws, st);
+  return causal ? launch_bwd_masked_t<E, 64, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws,
+                                                              st)
+                : launch_bwd_masked_t<E, 64, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                               ws, st);
+}
+
+hipError_t launch_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                             int left, int right, void* ws, bool fp16, hipStream_t st) {
+  return fp16 ? launch_bwd_window_e<_Float16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, left, right, ws, st)
+              : launch_bwd_window_e<__bf16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, left, right, ws, st);
 }
 
 hipError_t launch_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                                  float scale, int causal, const unsigned char* bm, int per_head, void* ws,
+                                  float scale, int causal, const unsigned char* bm, int per_head, void* ws, bool fp16,
                                   hipStream_t st) {
-  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
-  const MaskArgs mk{-1, -1, bm, per_head ? (long long)nb * nb : 0, nb, H};
-  if (d == 96)
-    return causal ? launch_bwd_masked_t<96, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
-                                                                 ws, st)
-                  : launch_bwd_masked_t<96, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
-                                                                  ws, st);
-  if (d == 128)
-    return causal ? launch_bwd_masked_t<128, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
-                                                                 ws, st)
-                  : launch_bwd_masked_t<128, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
-                                                                  ws, st);
-  return causal ? launch_bwd_masked_t<64, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws,
-                                                              st)
-                : launch_bwd_masked_t<64, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
-                                                               ws, st);
+  return fp16 ? launch_bwd_blocksparse_e<_Float16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, bm,
+                                                    per_head, ws, st)
+              : launch_bwd_blocksparse_e<__bf16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, bm,
+                                                 per_head, ws, st);
 }
 
 hipError_t launch_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -562,43 +562,51 @@ hipError_t launch_fwd_fp16(const void* q, const void* k, const void* v, void* o,
   return launch_fwd_e<_Float16>(q, k, v, o, lse, B, H, N, d, scale, causal, st);
 }
 
-// Forward with dropout on P (bf16): the plain forward's tiles and launch
-// shape, with the keep bits of each tile drawn in the kernel.
-template <int D, bool CAUSAL>
+// Forward with dropout on P: the plain forward's tiles and launch shape, with
+// the keep bits of each tile drawn in the kernel.
+template <typename E, int D, bool CAUSAL>
 static hipError_t launch_fwd_dropout_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                        int H, int N, float scale, const DropArgs& dp, hipStream_t st) {
   const long long G8 = (long long)B * H * ((N + FwdTile<D, 8>::BR - 1) / FwdTile<D, 8>::BR);
   if constexpr (D == 128)
-    if (!CAUSAL && G8 >= kNumCUs) return launch_fwd_nw<__bf16, D, CAUSAL, 8, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
-  return launch_fwd_nw<__bf16, D, CAUSAL, 4, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
+    if (!CAUSAL && G8 >= kNumCUs) return launch_fwd_nw<E, D, CAUSAL, 8, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
+  return launch_fwd_nw<E, D, CAUSAL, 4, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
+}
+
+template <typename E>
+static hipError_t launch_fwd_dropout_e(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                       int H, int N, int d, float scale, int causal, float p,
+                                       unsigned long long seed, hipStream_t st) {
+  const DropArgs dp = make_drop_args(p, seed);
+  if (d == 96) return causal ? launch_fwd_dropout_t<E, 96, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
+                              : launch_fwd_dropout_t<E, 96, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
+  if (d == 256) return causal ? launch_fwd_dropout_t<E, 256, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
+                              : launch_fwd_dropout_t<E, 256, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
+  if (d == 128) return causal ? launch_fwd_dropout_t<E, 128, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
+                              : launch_fwd_dropout_t<E, 128, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
+  return causal ? launch_fwd_dropout_t<E, 64, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
+                : launch_fwd_dropout_t<E, 64, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
 }
 
 hipError_t launch_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                              int N, int d, float scale, int causal, float p, unsigned long long seed,
+                              int N, int d, float scale, int causal, float p, unsigned long long seed, bool fp16,
                               hipStream_t st) {
-  const DropArgs dp = make_drop_args(p, seed);
-  if (d == 96) return causal ? launch_fwd_dropout_t<96, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
-                              : launch_fwd_dropout_t<96, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
-  if (d == 256) return causal ? launch_fwd_dropout_t<256, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
-                              : launch_fwd_dropout_t<256, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
-  if (d == 128) return causal ? launch_fwd_dropout_t<128, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
-                              : launch_fwd_dropout_t<128, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
-  return causal ? launch_fwd_dropout_t<64, true>(q, k, v, o, lse, B, H, N, scale, dp, st)
-                : launch_fwd_dropout_t<64, false>(q, k, v, o, lse, B, H, N, scale, dp, st);
+  return fp16 ? launch_fwd_dropout_e<_Float16>(q, k, v, o, lse, B, H, N, d, scale, causal, p, seed, st)
+              : launch_fwd_dropout_e<__bf16>(q, k, v, o, lse, B, H, N, d, scale, causal, p, seed, st);
 }
 
 // ---------------------------------------------------------------------------
 // Eq. (2) merge of S parts: for each row, with M = max_s LSE_s and
-// w_s = e^(LSE_s - M): O = sum_s w_s O_s / sum_s w_s (rounded once to bf16)
+// w_s = e^(LSE_s - M): O = sum_s w_s O_s / sum_s w_s (rounded once to E)
 // and LSE = M + ln sum_s w_s.  Parts with LSE_s = -inf weigh 0; a row whose
 // parts are all -inf gets O = 0, LSE = -inf.  HBM-bound: D/8 lanes per row,
 // each lane reads 8 consecutive floats of every part (two 16-byte loads) and
-// writes 8 bf16 (one 16-byte store).
+// writes 8 16-bit values (one 16-byte store).
 // ---------------------------------------------------------------------------
-template <int D>
+template <typename E, int D>
 __global__ void __launch_bounds__(256)
 lse_merge_kernel(const float* __restrict__ OP, const float* __restrict__ LP, int S,
-                 __bf16* __restrict__ O, float* __restrict__ LSE, long long rows) {
+                 E* __restrict__ O, float* __restrict__ LSE, long long rows) {
   constexpr int LPR = D / 8;  // lanes per row
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = t / LPR;
@@ -642,41 +650,41 @@ lse_merge_kernel(const float* __restrict__ OP, const float* __restrict__ LP, int
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   u32x4 w;
-  w[0] = pack_bf16x2(a0[0] * inv, a0[1] * inv);
-  w[1] = pack_bf16x2(a0[2] * inv, a0[3] * inv);
-  w[2] = pack_bf16x2(a1[0] * inv, a1[1] * inv);
-  w[3] = pack_bf16x2(a1[2] * inv, a1[3] * inv);
+  w[0] = pack2<E>(a0[0] * inv, a0[1] * inv);
+  w[1] = pack2<E>(a0[2] * inv, a0[3] * inv);
+  w[2] = pack2<E>(a1[0] * inv, a1[1] * inv);
+  w[3] = pack2<E>(a1[2] * inv, a1[3] * inv);
   *reinterpret_cast<u32x4*>(O + row * D + sub * 8) = w;
   if (sub == 0) LSE[row] = L > 0.f ? M + log2_fast(L) * kLn2 : -INFINITY;
 }
 
-hipError_t launch_lse_merge(const float* op, const float* lp, int S, void* o, float* lse, int B, int H, int N,
-                            int d, hipStream_t st) {
+template <typename E>
+static hipError_t launch_lse_merge_e(const float* op, const float* lp, int S, void* o, float* lse, int B, int H,
+                                     int N, int d, hipStream_t st) {
   const long long rows = (long long)B * H * N;
   const long long threads = rows * (d / 8);
   const long long blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (d == 256)
-    hipLaunchKernelGGL((lse_merge_kernel<256>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
-                       lse, rows);
-  else if (d == 96)
-    hipLaunchKernelGGL((lse_merge_kernel<96>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
-                       lse, rows);
-  else if (d == 128)
-    hipLaunchKernelGGL((lse_merge_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
-                       lse, rows);
-  else
-    hipLaunchKernelGGL((lse_merge_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, op, lp, S, (__bf16*)o,
-                       lse, rows);
+  const dim3 g((unsigned)blocks), b(256);
+  if (d == 256) hipLaunchKernelGGL((lse_merge_kernel<E, 256>), g, b, 0, st, op, lp, S, (E*)o, lse, rows);
+  else if (d == 96) hipLaunchKernelGGL((lse_merge_kernel<E, 96>), g, b, 0, st, op, lp, S, (E*)o, lse, rows);
+  else if (d == 128) hipLaunchKernelGGL((lse_merge_kernel<E, 128>), g, b, 0, st, op, lp, S, (E*)o, lse, rows);
+  else hipLaunchKernelGGL((lse_merge_kernel<E, 64>), g, b, 0, st, op, lp, S, (E*)o, lse, rows);
   return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const float* op, const float* lp, int S, void* o, float* lse, int B, int H, int N,
+                            int d, bool fp16, hipStream_t st) {
+  return fp16 ? launch_lse_merge_e<_Float16>(op, lp, S, o, lse, B, H, N, d, st)
+              : launch_lse_merge_e<__bf16>(op, lp, S, o, lse, B, H, N, d, st);
 }
 
 // Key-split forward: S parts per query block (four-wave workgroups), then the
 // merge.  S == 1 is the plain forward.
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                      int H, int N, float scale, int S, void* ws, hipStream_t st) {
-  if (S <= 1) return launch_fwd_t<__bf16, D, CAUSAL>(q, k, v, o, lse, B, H, N, scale, st);
+  if (S <= 1) return launch_fwd_t<E, D, CAUSAL>(q, k, v, o, lse, B, H, N, scale, st);
   using T = FwdTile<D, 4>;
   const SplitLayout w = split_workspace_layout(Shape{B, H, N, D}, S);
   const int Tr = (N + T::BR - 1) / T::BR;
@@ -686,67 +694,90 @@ static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v
   char* base = reinterpret_cast<char*>(ws);
   SplitArgs sp{S, (Tc + S - 1) / S, reinterpret_cast<float*>(base + w.o_parts),
                reinterpret_cast<float*>(base + w.lse_parts), (long long)B * H * N * D, (long long)B * H * N};
-  hipLaunchKernelGGL((fwd_kernel<__bf16, D, CAUSAL, 4, true, kMaskDense, false>), dim3((unsigned)G), dim3(T::NT), 0,
-                     st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
-                     scale * kLog2e, sp, MaskArgs{}, DropArgs{});
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, 4, true, kMaskDense, false>), dim3((unsigned)G), dim3(T::NT), 0,
+                     st, (const E*)q, (const E*)k, (const E*)v, (E*)o, lse, N, Tr, scale * kLog2e, sp, MaskArgs{},
+                     DropArgs{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_lse_merge(sp.OP, sp.LP, S, o, lse, B, H, N, D, st);
+  return launch_lse_merge_e<E>(sp.OP, sp.LP, S, o, lse, B, H, N, D, st);
+}
+
+template <typename E>
+static hipError_t launch_fwd_splitkv_e(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                       int H, int N, int d, float scale, int causal, int S, void* ws,
+                                       hipStream_t st) {
+  if (d == 96) return causal ? launch_fwd_split_t<E, 96, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
+                              : launch_fwd_split_t<E, 96, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
+  if (d == 256) return causal ? launch_fwd_split_t<E, 256, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
+                              : launch_fwd_split_t<E, 256, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
+  if (d == 128) return causal ? launch_fwd_split_t<E, 128, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
+                              : launch_fwd_split_t<E, 128, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
+  return causal ? launch_fwd_split_t<E, 64, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
+                : launch_fwd_split_t<E, 64, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
 }
 
 hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                              int N, int d, float scale, int causal, int S, void* ws, hipStream_t st) {
-  if (d == 96) return causal ? launch_fwd_split_t<96, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
-                              : launch_fwd_split_t<96, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
-  if (d == 256) return causal ? launch_fwd_split_t<256, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
-                              : launch_fwd_split_t<256, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
-  if (d == 128) return causal ? launch_fwd_split_t<128, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
-                              : launch_fwd_split_t<128, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
-  return causal ? launch_fwd_split_t<64, true>(q, k, v, o, lse, B, H, N, scale, S, ws, st)
-                : launch_fwd_split_t<64, false>(q, k, v, o, lse, B, H, N, scale, S, ws, st);
+                              int N, int d, float scale, int causal, int S, void* ws, bool fp16, hipStream_t st) {
+  return fp16 ? launch_fwd_splitkv_e<_Float16>(q, k, v, o, lse, B, H, N, d, scale, causal, S, ws, st)
+              : launch_fwd_splitkv_e<__bf16>(q, k, v, o, lse, B, H, N, d, scale, causal, S, ws, st);
 }
 
 // Sliding-window and block-sparse forwards: four-wave workgroups (128 rows,
 // two 64-row mask blocks), the same kernel with a per-tile predicate.
-template <int D, bool CAUSAL, int MODE>
+template <typename E, int D, bool CAUSAL, int MODE>
 static hipError_t launch_fwd_masked_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                       int H, int N, float scale, const MaskArgs& mk, hipStream_t st) {
   using T = FwdTile<D, 4>;
   const int Tr = (N + T::BR - 1) / T::BR;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<__bf16, D, CAUSAL, 4, false, MODE, false>), dim3((unsigned)G), dim3(T::NT), 0,
-                     st, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, N, Tr,
-                     scale * kLog2e, SplitArgs{1, 0, nullptr, nullptr, 0, 0}, mk, DropArgs{});
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, 4, false, MODE, false>), dim3((unsigned)G), dim3(T::NT), 0, st,
+                     (const E*)q, (const E*)k, (const E*)v, (E*)o, lse, N, Tr, scale * kLog2e,
+                     SplitArgs{1, 0, nullptr, nullptr, 0, 0}, mk, DropArgs{});
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-                             int d, float scale, int left, int right, hipStream_t st) {
+template <typename E>
+static hipError_t launch_fwd_window_e(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                      int H, int N, int d, float scale, int left, int right, hipStream_t st) {
   // a bound of N - 1 or more limits nothing: the same as no bound
   const MaskArgs mk{left >= N - 1 ? -1 : left, right >= N - 1 ? -1 : right, nullptr, 0, 0, H};
-  if (d == 96) return launch_fwd_masked_t<96, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
-  if (d == 256) return launch_fwd_masked_t<256, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
-  if (d == 128) return launch_fwd_masked_t<128, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
-  return launch_fwd_masked_t<64, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  if (d == 96) return launch_fwd_masked_t<E, 96, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  if (d == 256) return launch_fwd_masked_t<E, 256, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  if (d == 128) return launch_fwd_masked_t<E, 128, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  return launch_fwd_masked_t<E, 64, false, kMaskWindow>(q, k, v, o, lse, B, H, N, scale, mk, st);
+}
+
+template <typename E>
+static hipError_t launch_fwd_blocksparse_e(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                           int H, int N, int d, float scale, int causal, const unsigned char* bm,
+                                           int per_head, hipStream_t st) {
+  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+  const MaskArgs mk{-1, -1, bm, per_head ? (long long)nb * nb : 0, nb, H};
+  if (d == 96)
+    return causal ? launch_fwd_masked_t<E, 96, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
+                  : launch_fwd_masked_t<E, 96, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  if (d == 256)
+    return causal ? launch_fwd_masked_t<E, 256, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
+                  : launch_fwd_masked_t<E, 256, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  if (d == 128)
+    return causal ? launch_fwd_masked_t<E, 128, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
+                  : launch_fwd_masked_t<E, 128, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
+  return causal ? launch_fwd_masked_t<E, 64, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
+                : launch_fwd_masked_t<E, 64, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
+}
+
+hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                             int d, float scale, int left, int right, bool fp16, hipStream_t st) {
+  return fp16 ? launch_fwd_window_e<_Float16>(q, k, v, o, lse, B, H, N, d, scale, left, right, st)
+              : launch_fwd_window_e<__bf16>(q, k, v, o, lse, B, H, N, d, scale, left, right, st);
 }
 
 hipError_t launch_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                   int N, int d, float scale, int causal, const unsigned char* bm, int per_head,
-                                  hipStream_t st) {
-  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
-  const MaskArgs mk{-1, -1, bm, per_head ? (long long)nb * nb : 0, nb, H};
-  if (d == 96)
-    return causal ? launch_fwd_masked_t<96, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
-                  : launch_fwd_masked_t<96, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
-  if (d == 256)
-    return causal ? launch_fwd_masked_t<256, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
-                  : launch_fwd_masked_t<256, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
-  if (d == 128)
-    return causal ? launch_fwd_masked_t<128, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
-                  : launch_fwd_masked_t<128, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
-  return causal ? launch_fwd_masked_t<64, true, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st)
-                : launch_fwd_masked_t<64, false, kMaskBlocks>(q, k, v, o, lse, B, H, N, scale, mk, st);
+                                  bool fp16, hipStream_t st) {
+  return fp16 ? launch_fwd_blocksparse_e<_Float16>(q, k, v, o, lse, B, H, N, d, scale, causal, bm, per_head, st)
+              : launch_fwd_blocksparse_e<__bf16>(q, k, v, o, lse, B, H, N, d, scale, causal, bm, per_head, st);
 }
 
 template <int D, bool CAUSAL>

@@ -49,6 +49,11 @@ SIGNATURES = {
                                     _c_float, _c_int, _vp, _c_int, _vp, _c_size_t, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
 }
+# the float16 versions of the key split, the merge, the masks and dropout take
+# the same arguments as the bf16 ones
+for _name in ("fa_fwd_splitkv", "fa_lse_merge", "fa_fwd_window", "fa_bwd_window", "fa_fwd_blocksparse",
+              "fa_bwd_blocksparse", "fa_fwd_dropout", "fa_bwd_dropout"):
+    SIGNATURES[_name + "_fp16"] = SIGNATURES[_name]
 
 
 class FAError(RuntimeError):
@@ -181,9 +186,21 @@ def splitkv_workspace_bytes(B: int, H: int, N: int, d: int, num_splits: int = 0)
     return int(load().fa_fwd_splitkv_workspace_bytes(B, H, N, d, int(num_splits)))
 
 
+def _half(q):
+    """The 16-bit element type of q (bf16 or float16); the entry points for float16 carry the suffix _fp16."""
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"unsupported dtype {q.dtype}: bf16 or float16")
+    return q.dtype
+
+
+def _sym(lib, name, dt):
+    full = name if dt == torch.bfloat16 else name + "_fp16"
+    return full, getattr(lib, full)
+
+
 def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0,
                 workspace=None, out=None, lse=None):
-    """bf16 forward with the keys split into parallel parts merged by Eq. (2); returns ``(o, lse)``.
+    """bf16 or float16 forward with the keys split into parallel parts merged by Eq. (2); returns ``(o, lse)``.
 
     ``num_splits <= 0`` lets the library choose.  ``workspace`` (uint8 GPU
     tensor of at least ``splitkv_workspace_bytes`` bytes) is allocated if not
@@ -193,14 +210,15 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     if q.dim() != 4:
         raise ValueError("q must be [B,H,N,d]")
     B, H, N, d = q.shape
+    dt = _half(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16, (B, H, N, d))
+        _check(t, n, dt, (B, H, N, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", torch.bfloat16, (B, H, N, d))
+        _check(out, "out", dt, (B, H, N, d))
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
@@ -210,47 +228,53 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _check(workspace, "workspace", torch.uint8)
-    st = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                            float(scale), int(bool(causal)), int(num_splits),
-                            workspace.data_ptr() if workspace is not None else None,
-                            workspace.numel() if workspace is not None else 0, _stream())
+    name, fn = _sym(lib, "fa_fwd_splitkv", dt)
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+            float(scale), int(bool(causal)), int(num_splits),
+            workspace.data_ptr() if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, _stream())
     if st != 0:
-        raise FAError(st, "fa_fwd_splitkv")
+        raise FAError(st, name)
     return out, lse
 
 
-def lse_merge(o_parts, lse_parts, out=None, lse=None):
+def lse_merge(o_parts, lse_parts, out=None, lse=None, dtype=torch.bfloat16):
     """Eq. (2) merge of ``o_parts`` float32 ``[S,B,H,N,d]`` and ``lse_parts`` float32 ``[S,B,H,N]``.
 
-    Returns ``(o, lse)``: bf16 ``[B,H,N,d]`` and float32 ``[B,H,N]``.
+    Returns ``(o, lse)``: ``dtype`` (bf16 or float16; that of ``out`` when given)
+    ``[B,H,N,d]`` and float32 ``[B,H,N]``.
     """
     lib = load()
+    dt = out.dtype if out is not None else dtype
+    if dt not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"unsupported output dtype {dt}")
     if o_parts.dim() != 5:
         raise ValueError("o_parts must be [S,B,H,N,d]")
     S, B, H, N, d = o_parts.shape
     _check(o_parts, "o_parts", torch.float32, (S, B, H, N, d))
     _check(lse_parts, "lse_parts", torch.float32, (S, B, H, N))
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=o_parts.device)
+        out = torch.empty((B, H, N, d), dtype=dt, device=o_parts.device)
     else:
-        _check(out, "out", torch.bfloat16, (B, H, N, d))
+        _check(out, "out", dt, (B, H, N, d))
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
     else:
         _check(lse, "lse", torch.float32, (B, H, N))
-    st = lib.fa_lse_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                          _stream())
+    name, fn = _sym(lib, "fa_lse_merge", dt)
+    st = fn(o_parts.data_ptr(), lse_parts.data_ptr(), S, out.data_ptr(), lse.data_ptr(), B, H, N, d, _stream())
     if st != 0:
-        raise FAError(st, "fa_lse_merge")
+        raise FAError(st, name)
     return out, lse
 
 
 def _fwd_outputs(q, out, lse):
     B, H, N, d = q.shape
+    dt = q.dtype
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", torch.bfloat16, (B, H, N, d))
+        _check(out, "out", dt, (B, H, N, d))
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
@@ -259,33 +283,36 @@ def _fwd_outputs(q, out, lse):
 
 
 def fwd_window(q, k, v, window_left: int, window_right: int, scale: float | None = None, out=None, lse=None):
-    """bf16 sliding-window forward: key j visible to query i iff i-left <= j <= i+right
+    """bf16 or float16 sliding-window forward: key j visible to query i iff i-left <= j <= i+right
     (negative = unlimited); returns ``(o, lse)``."""
     lib = load()
     if q.dim() != 4:
         raise ValueError("q must be [B,H,N,d]")
     B, H, N, d = q.shape
+    dt = _half(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16, (B, H, N, d))
+        _check(t, n, dt, (B, H, N, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _fwd_outputs(q, out, lse)
-    st = lib.fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                           float(scale), int(window_left), int(window_right), _stream())
+    name, fn = _sym(lib, "fa_fwd_window", dt)
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+            float(scale), int(window_left), int(window_right), _stream())
     if st != 0:
-        raise FAError(st, "fa_fwd_window")
+        raise FAError(st, name)
     return out, lse
 
 
 def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """bf16 block-sparse forward over 64 x 64 blocks; ``block_mask`` is a uint8 GPU tensor
+    """bf16 or float16 block-sparse forward over 64 x 64 blocks; ``block_mask`` is a uint8 GPU tensor
     ``[H, nb, nb]`` or ``[nb, nb]`` (shared by all heads), nb = ceil(N/64); returns ``(o, lse)``."""
     lib = load()
     if q.dim() != 4:
         raise ValueError("q must be [B,H,N,d]")
     B, H, N, d = q.shape
+    dt = _half(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16, (B, H, N, d))
+        _check(t, n, dt, (B, H, N, d))
     nb = (N + 63) // 64
     if block_mask.dim() == 3:
         _check(block_mask, "block_mask", torch.uint8, (H, nb, nb))
@@ -296,18 +323,20 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _fwd_outputs(q, out, lse)
-    st = lib.fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
-                                d, float(scale), int(bool(causal)), block_mask.data_ptr(), per_head, _stream())
+    name, fn = _sym(lib, "fa_fwd_blocksparse", dt)
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
+            d, float(scale), int(bool(causal)), block_mask.data_ptr(), per_head, _stream())
     if st != 0:
-        raise FAError(st, "fa_fwd_blocksparse")
+        raise FAError(st, name)
     return out, lse
 
 
 def _bwd_args(q, k, v, o, lse, do, scale, workspace, out):
-    """Shared checks and allocations of the bf16 masked backward calls."""
+    """Shared checks and allocations of the masked backward calls (bf16 or float16)."""
     B, H, N, d = q.shape
+    dt = _half(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, n, torch.bfloat16, (B, H, N, d))
+        _check(t, n, dt, (B, H, N, d))
     _check(lse, "lse", torch.float32, (B, H, N))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -319,27 +348,30 @@ def _bwd_args(q, k, v, o, lse, do, scale, workspace, out):
     else:
         dq, dk, dv = out
         for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-            _check(t, n, torch.bfloat16, (B, H, N, d))
+            _check(t, n, dt, (B, H, N, d))
     return (B, H, N, d), float(scale), workspace, (dq, dk, dv)
 
 
 def bwd_window(q, k, v, o, lse, do, window_left: int, window_right: int, scale: float | None = None,
                workspace=None, out=None):
-    """bf16 backward of ``fwd_window`` (``fa_bwd_window``); returns ``(dq, dk, dv)``."""
+    """bf16 or float16 backward of ``fwd_window`` (``fa_bwd_window``); returns ``(dq, dk, dv)``."""
     lib = load()
+    dt = _half(q)
     (B, H, N, d), scale, workspace, (dq, dk, dv) = _bwd_args(q, k, v, o, lse, do, scale, workspace, out)
-    st = lib.fa_bwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, int(window_left),
-                           int(window_right), workspace.data_ptr(), workspace.numel(), _stream())
+    name, fn = _sym(lib, "fa_bwd_window", dt)
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, int(window_left),
+            int(window_right), workspace.data_ptr(), workspace.numel(), _stream())
     if st != 0:
-        raise FAError(st, "fa_bwd_window")
+        raise FAError(st, name)
     return dq, dk, dv
 
 
 def bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal: bool = False, scale: float | None = None,
                     workspace=None, out=None):
-    """bf16 backward of ``fwd_blocksparse`` (``fa_bwd_blocksparse``); returns ``(dq, dk, dv)``."""
+    """bf16 or float16 backward of ``fwd_blocksparse`` (``fa_bwd_blocksparse``); returns ``(dq, dk, dv)``."""
     lib = load()
+    dt = _half(q)
     (B, H, N, d), scale, workspace, (dq, dk, dv) = _bwd_args(q, k, v, o, lse, do, scale, workspace, out)
     nb = (N + 63) // 64
     if block_mask.dim() == 3:
@@ -348,41 +380,45 @@ def bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal: bool = False, scale
     else:
         _check(block_mask, "block_mask", torch.uint8, (nb, nb))
         per_head = 0
-    st = lib.fa_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale,
-                                int(bool(causal)), block_mask.data_ptr(), per_head, workspace.data_ptr(),
-                                workspace.numel(), _stream())
+    name, fn = _sym(lib, "fa_bwd_blocksparse", dt)
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale,
+            int(bool(causal)), block_mask.data_ptr(), per_head, workspace.data_ptr(),
+            workspace.numel(), _stream())
     if st != 0:
-        raise FAError(st, "fa_bwd_blocksparse")
+        raise FAError(st, name)
     return dq, dk, dv
 
 
 def fwd_dropout(q, k, v, dropout_p: float, seed: int, causal: bool = False, scale: float | None = None,
                 out=None, lse=None):
-    """bf16 forward with dropout on P (Philox4x32-10 mask from ``seed``); returns ``(o, lse)``."""
+    """bf16 or float16 forward with dropout on P (Philox4x32-10 mask from ``seed``); returns ``(o, lse)``."""
     lib = load()
     if q.dim() != 4:
         raise ValueError("q must be [B,H,N,d]")
     B, H, N, d = q.shape
+    dt = _half(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16, (B, H, N, d))
+        _check(t, n, dt, (B, H, N, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _fwd_outputs(q, out, lse)
-    st = lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                            float(scale), int(bool(causal)), float(dropout_p), int(seed) & (2**64 - 1), _stream())
+    name, fn = _sym(lib, "fa_fwd_dropout", dt)
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+            float(scale), int(bool(causal)), float(dropout_p), int(seed) & (2**64 - 1), _stream())
     if st != 0:
-        raise FAError(st, "fa_fwd_dropout")
+        raise FAError(st, name)
     return out, lse
 
 
 def bwd_dropout(q, k, v, o, lse, do, dropout_p: float, seed: int, causal: bool = False,
                 scale: float | None = None, workspace=None, out=None):
-    """bf16 backward through the same dropout mask as ``fwd_dropout``; returns ``(dq, dk, dv)``."""
+    """bf16 or float16 backward through the same dropout mask as ``fwd_dropout``; returns ``(dq, dk, dv)``."""
     lib = load()
     B, H, N, d = q.shape
+    dt = _half(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, n, torch.bfloat16, (B, H, N, d))
+        _check(t, n, dt, (B, H, N, d))
     _check(lse, "lse", torch.float32, (B, H, N))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -395,11 +431,12 @@ def bwd_dropout(q, k, v, o, lse, do, dropout_p: float, seed: int, causal: bool =
     else:
         dq, dk, dv = out
         for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-            _check(t, n, torch.bfloat16, (B, H, N, d))
-    st = lib.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
-                            float(dropout_p), int(seed) & (2**64 - 1), workspace.data_ptr(), workspace.numel(),
-                            _stream())
+            _check(t, n, dt, (B, H, N, d))
+    name, fn = _sym(lib, "fa_bwd_dropout", dt)
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+            float(dropout_p), int(seed) & (2**64 - 1), workspace.data_ptr(), workspace.numel(),
+            _stream())
     if st != 0:
-        raise FAError(st, "fa_bwd_dropout")
+        raise FAError(st, name)
     return dq, dk, dv

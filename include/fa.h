@@ -275,6 +275,47 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
                        int causal, const unsigned char* block_mask, int mask_per_head, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fp16 versions of the key split, the merge, the masks and dropout:
+ * fa_fwd_splitkv_fp16, fa_lse_merge_fp16, fa_fwd_window_fp16,
+ * fa_bwd_window_fp16, fa_fwd_blocksparse_fp16, fa_bwd_blocksparse_fp16,
+ * fa_fwd_dropout_fp16, fa_bwd_dropout_fp16.  Each has exactly the parameter
+ * list, preconditions, errors and ownership of the entry point without the
+ * suffix, with every [B][H][N][d] 16-bit tensor (q, k, v, o, dO, dq, dk, dv)
+ * in IEEE binary16 (_Float16) instead of bf16, as fa_fwd_fp16 / fa_bwd_fp16
+ * do for fa_fwd / fa_bwd (FlashAttention optimisation page, section 6.2: FP16
+ * or BF16 storage).  lse, the fp32 parts of the key split and the workspaces
+ * are unchanged (fa_fwd_splitkv_workspace_bytes and fa_bwd_workspace_bytes
+ * give their sizes).  P and dS are rounded to fp16 for the MFMAs; the result
+ * is rounded once to fp16 (round to nearest even).
+ */
+int fa_fwd_splitkv_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int N, int d, float scale, int causal, int num_splits,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_lse_merge_fp16(const float* o_parts, const float* lse_parts, int num_parts, void* o, float* lse,
+                      int B, int H, int N, int d, hipStream_t stream);
+int fa_fwd_window_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, float scale, int window_left, int window_right,
+                       hipStream_t stream);
+int fa_bwd_window_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                       int window_left, int window_right, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+int fa_fwd_blocksparse_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int N, int d, float scale, int causal,
+                            const unsigned char* block_mask, int mask_per_head, hipStream_t stream);
+int fa_bwd_blocksparse_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                            int causal, const unsigned char* block_mask, int mask_per_head, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+int fa_fwd_dropout_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int N, int d, float scale, int causal, float dropout_p,
+                        unsigned long long seed, hipStream_t stream);
+int fa_bwd_dropout_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                        int causal, float dropout_p, unsigned long long seed, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* fa_status_string - static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

@@ -42,7 +42,9 @@ def test_header_declares_the_boundary():
                                            "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_bytes",
                                            "fa_fwd_splitkv", "fa_lse_merge", "fa_fwd_window",
                                            "fa_fwd_blocksparse", "fa_bwd_window", "fa_bwd_blocksparse",
-                                           "fa_status_string"])
+                                           "fa_fwd_splitkv_fp16", "fa_lse_merge_fp16", "fa_fwd_window_fp16",
+                                           "fa_bwd_window_fp16", "fa_fwd_blocksparse_fp16", "fa_bwd_blocksparse_fp16",
+                                           "fa_fwd_dropout_fp16", "fa_bwd_dropout_fp16", "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
