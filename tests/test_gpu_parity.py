@@ -204,6 +204,24 @@ def test_ragged_bf16_many_heads(gpu_lib, N, d, causal):
     check_lse(f"ragged_bf16_many_heads N={N} d={d} causal={causal}", _np(lse), rl)
 
 
+@pytest.mark.parametrize("H,N", [(8, 300), (128, 200), (128, 600)])
+@pytest.mark.parametrize("d", [96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_each_workgroup_width(gpu_lib, H, N, d, causal):
+    """At d = 96 and 128 the forward picks its workgroup height from the grid
+    size: B1 H8 N300 leaves CUs idle with 128-row blocks (24 blocks) and runs
+    64-row blocks, B1 H128 N200 fills the 256 CUs with 128-row blocks but not
+    with 256-row ones, and B1 H128 N600 fills them with 256-row blocks.
+    Each width, with a ragged last block, is compared in full."""
+    q, k, v = make_inputs(1, H, N, d, "bf16", seed=800 + H + N + d)
+    scale = d ** -0.5
+    o, lse = _fwd(gpu_lib, q, k, v, causal, scale)
+    ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), scale, causal)
+    name = f"each_workgroup_width H={H} N={N} d={d} causal={causal}"
+    check_o(name, _np(o), ro)
+    check_lse(name, _np(lse), rl)
+
+
 def test_forward_deterministic(gpu_lib):
     q, k, v = _gpu(*make_inputs(2, 4, 1000, 128, "bf16", seed=7))
     o1, l1 = gpu_lib.fwd(q, k, v, causal=True)
