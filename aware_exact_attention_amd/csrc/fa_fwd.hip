@@ -10,8 +10,8 @@
 // Software 2026(1) p.218 survey.  The per-row statistic written for the
 // backward pass is LSE = m + ln(l).
 //
-// gfx950 mapping of the bf16 kernel (one workgroup = 4 or 8 waves = 128 or
-// 256 query rows, two waves per SIMD either way):
+// gfx950 mapping of the bf16 kernel (one workgroup = 2, 4 or 8 waves = 64,
+// 128 or 256 query rows of one head):
 //  * each wave owns 32 whole query rows, so the row statistics m and l never
 //    leave the wave (no inter-wave exchange);
 //  * the wave computes S^T = K_j Q_i^T with v_mfma_f32_32x32x16_bf16: the
@@ -21,10 +21,11 @@
 //  * it then computes O^T += V_j^T P^T, which again keeps one query per lane,
 //    so rescaling and the final division are in-lane; P^T is fed to the MFMA
 //    straight from the score registers (rounded to bf16), never via memory;
-//  * the Q fragment stays in VGPRs for the whole KV sweep; K_j is staged in
-//    LDS row-major and V_j transposed (V^T), both with XOR swizzles that keep
-//    the 128-bit LDS reads of a wave free of bank conflicts, and both double
-//    buffered so the HBM loads of tile j+1 overlap the MFMAs of tile j;
+//  * the Q fragment stays in VGPRs for the whole KV sweep; K_j and V_j are
+//    copied from HBM straight into LDS, row-major under one XOR swizzle that
+//    keeps both the 128-bit K row reads and the transposing V^T reads
+//    (ds_read_b64_tr_b16) free of bank conflicts, and double buffered so the
+//    loads of tile j+1 overlap the MFMAs of tile j;
 //  * the exponentials are exp2 with scale*log2(e) folded into one FMA.
 #include "fa_common.h"
 #include "fa_validate.h"

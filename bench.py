@@ -214,14 +214,14 @@ def config_rows():
 
 
 def next_rows():
-    """Key-split forward (fa_fwd_splitkv) against fa_fwd on grids too small to fill
-    the GPU, the sliding-window and block-sparse forwards, fp16 inputs, dropout,
+    """Key-split forward (fa_fwd_splitkv) against fa_fwd, and fa_bwd, on grids too
+    small to fill the GPU, the sliding-window and block-sparse forwards, fp16 inputs, dropout,
     and the Eq. (2) merge kernel (fa_lse_merge) against the HBM roof."""
     res = {}
     for name, (B, H, N, d, causal) in {"B1H8N2048d128": (1, 8, 2048, 128, False),
                                        "B1H4N4096d128_causal": (1, 4, 4096, 128, True),
                                        "B1H2N8192d64": (1, 2, 8192, 64, False)}.items():
-        q, k, v = (t.cuda() for t in make_inputs(B, H, N, d, "bf16", 9, 1.0))
+        q, k, v, do = (t.cuda() for t in make_inputs(B, H, N, d, "bf16", 9, 1.0, backward=True))
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
         parts = fa.splitkv_parts(B, H, N, d, 0)
@@ -230,9 +230,14 @@ def next_rows():
         t_f = _graph_ms(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse), 20)
         t_s = _graph_ms(lambda: fa.fwd_splitkv(q, k, v, causal=causal, workspace=ws, out=o, lse=lse), 20)
         assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+        # the backward of these small grids runs its dK/dV and dQ passes in one launch
+        wsb = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+        t_b = _graph_ms(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, workspace=wsb, out=grads), 20)
         res[name] = {"parts": parts, "fa_fwd_ms": round(t_f, 5), "fa_fwd_splitkv_ms": round(t_s, 5),
                      "speedup": round(t_f / t_s, 3), "splitkv_tflops": round(flop / (t_s * 1e-3) / 1e12, 1),
-                     "splitkv_frac_peak": round(flop / (t_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                     "splitkv_frac_peak": round(flop / (t_s * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "fa_bwd_ms": round(t_b, 5), "bwd_tflops": round(2.5 * flop / (t_b * 1e-3) / 1e12, 1)}
     # tile-skipping masks at the benchmark shape: FLOP counted on the visible (query, key) pairs only
     B, H, N, d = 1, 8, 16384, 128
     q, k, v = (t.cuda() for t in make_inputs(B, H, N, d, "bf16", 9, 1.0))

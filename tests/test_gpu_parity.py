@@ -285,6 +285,24 @@ def test_bwd_small(gpu_lib, N, d, causal):
     check_grad(tag, "dV", dv, rv)
 
 
+@pytest.mark.parametrize("H,N", [(2, 300), (64, 256), (128, 200)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_each_launch_shape(gpu_lib, H, N, d, causal):
+    """The backward runs its two passes in one grid when both fit on the 256
+    CUs together (128-key and 128-query blocks: B1 H2 N300 with 6 + 6
+    workgroups, B1 H64 N256 with exactly 128 + 128) and as two launches
+    otherwise (B1 H128 N200: 256 + 256).  Each shape is compared in full."""
+    q, k, v, do = make_inputs(1, H, N, d, "bf16", seed=900 + H + N + d, backward=True)
+    scale = d ** -0.5
+    _, _, dq, dk, dv = _bwd_case(gpu_lib, q, k, v, do, causal, scale)
+    rq, rk, rv = oracle.ref_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal)
+    tag = f"bwd_each_launch_shape H={H} N={N} d={d} causal={causal}"
+    check_grad(tag, "dQ", dq, rq)
+    check_grad(tag, "dK", dk, rk)
+    check_grad(tag, "dV", dv, rv)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_ragged_many_heads(gpu_lib, causal):
     """256 heads of 300 rows: a grid large enough for the 256-row dQ
