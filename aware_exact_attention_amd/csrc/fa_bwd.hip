@@ -177,9 +177,16 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses for the direct loads
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int tile = xcd_remap(bid, nblk);
-  const int bh = tile / Tk;
-  const int jt = tile - bh * Tk;  // causal: key block 0 has the most query steps and is dispatched first
+  int bh, jt;
+  if (CAUSAL) {
+    // key block jt sees the query steps from its diagonal on: block 0 has the
+    // most, so the blocks go out longest first across all heads
+    causal_order(bid, nblk / Tk, Tk, bh, jt);
+  } else {
+    const int tile = xcd_remap(bid, nblk);
+    bh = tile / Tk;
+    jt = tile - bh * Tk;
+  }
   const int k0 = jt * T::BKV;
   const size_t head = size_t(bh) * N * D;
   const int head_bytes = N * T::GRS;

@@ -273,8 +273,9 @@ __device__ __forceinline__ int xcd_remap(int w, int G) {
   return (w & 7) * (G >> 3) + (w >> 3);
 }
 
-// Causal query-major grids (BH heads x T row blocks, block rank r of a head
-// has T - r key tiles): block w -> (head bh, rank r, 0 = the head's longest).
+// Causal grids (BH heads x T blocks, block rank r of a head has T - r units
+// of work: key tiles of a query block, or query steps of a key block):
+// block w -> (head bh, rank r, 0 = the head's longest).
 // When BH is a multiple of the 8 XCDs, XCD x = w % 8 takes the heads
 // bh = x (mod 8) -- their K and V stay in that XCD's L2 -- and dispatches
 // its blocks longest first over all of those heads, so that the short blocks

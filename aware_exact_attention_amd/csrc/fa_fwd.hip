@@ -570,8 +570,9 @@ hipError_t launch_fwd_fp16(const void* q, const void* k, const void* v, void* o,
   return launch_fwd_e<_Float16>(q, k, v, o, lse, B, H, N, d, scale, causal, st);
 }
 
-// Forward with dropout on P: the plain forward's tiles and launch shape, with
-// the keep bits of each tile drawn in the kernel.
+// Forward with dropout on P: the plain forward's tiles, with the keep bits of
+// each tile drawn in the kernel; eight-wave workgroups for non-causal d = 128
+// grids that cover every CU, four waves otherwise.
 template <typename E, int D, bool CAUSAL>
 static hipError_t launch_fwd_dropout_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                        int H, int N, float scale, const DropArgs& dp, hipStream_t st) {
