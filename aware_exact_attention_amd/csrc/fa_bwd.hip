@@ -831,14 +831,17 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                      (const float*)lse2, (const float*)Dv, (E*)dk, (E*)dv, dp, N, Tk, c, scale, MaskArgs{});
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (dq8)
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 8, DROP, kMaskDense>), dim3((unsigned)Gq), dim3(DqTile<D, 8>::NT),
-                       0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
-                       (const float*)lse2, (const float*)Dv, (E*)dq, dp, N, Tr, c, scale, MaskArgs{});
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 4, DROP, kMaskDense>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT),
-                       0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
-                       (const float*)lse2, (const float*)Dv, (E*)dq, dp, N, Tr, c, scale, MaskArgs{});
+  if constexpr (D == 128 || D == 96) {
+    if (dq8) {
+      hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 8, DROP, kMaskDense>), dim3((unsigned)Gq),
+                         dim3(DqTile<D, 8>::NT), 0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
+                         (const float*)lse2, (const float*)Dv, (E*)dq, dp, N, Tr, c, scale, MaskArgs{});
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 4, DROP, kMaskDense>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT), 0,
+                     st, (const E*)q, (const E*)k, (const E*)v, (const E*)dO, (const float*)lse2, (const float*)Dv,
+                     (E*)dq, dp, N, Tr, c, scale, MaskArgs{});
   return hipGetLastError();
 }
 
@@ -846,6 +849,9 @@ template <typename E>
 static hipError_t launch_bwd_e(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                                int causal, void* ws, hipStream_t st) {
+  if (d == 256)
+    return causal ? launch_bwd_t<E, 256, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st)
+                  : launch_bwd_t<E, 256, false>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st);
   if (d == 96)
     return causal ? launch_bwd_t<E, 96, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st)
                   : launch_bwd_t<E, 96, false>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st);

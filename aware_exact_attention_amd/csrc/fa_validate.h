@@ -36,7 +36,7 @@ inline int64_t tensor_elems(const Shape& s) {
 }
 
 // Head dimensions: 64, 96 and 128 everywhere; 256 on the forward entry points
-// only (allow256).
+// and the plain backward (fa_bwd, fa_bwd_fp16): allow256.
 inline bool head_dim_ok(int d, bool allow256) { return d == 64 || d == 96 || d == 128 || (allow256 && d == 256); }
 
 inline int check_common(const Shape& s, float scale, int causal, bool allow256 = false) {
@@ -79,7 +79,7 @@ struct BwdWorkspace {
 
 inline BwdWorkspace bwd_workspace_layout(const Shape& s) {
   const int64_t n = tensor_elems(s);
-  if (n < 0 || !head_dim_ok(s.d, false)) return BwdWorkspace{0, 0, 0};
+  if (n < 0 || !head_dim_ok(s.d, true)) return BwdWorkspace{0, 0, 0};
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t rows = size_t(s.B) * s.H * s.N;
   BwdWorkspace w;
@@ -94,9 +94,9 @@ inline size_t bwd_workspace_bytes(const Shape& s) { return bwd_workspace_layout(
 inline int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
                         const void* dO, const void* dq, const void* dk, const void* dv,
                         const Shape& s, float scale, int causal,
-                        const void* ws, size_t ws_bytes) {
+                        const void* ws, size_t ws_bytes, bool allow256 = false) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return kErrNull;
-  int st = check_common(s, scale, causal);
+  int st = check_common(s, scale, causal, allow256);
   if (st != kOk) return st;
   const void* all[9] = {q, k, v, o, lse, dO, dq, dk, dv};
   for (const void* p : all)

@@ -301,15 +301,20 @@ def next_rows():
         "bwd_ms": round(t_b96, 5), "bwd_tflops": round(2.5 * fl_96 / (t_b96 * 1e-3) / 1e12, 1),
         "bwd_frac_peak": round(2.5 * fl_96 / (t_b96 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     del q96, k96, v96, do96, o96, g96, ws96
-    # head dimension 256 (forward only: one wave per SIMD) at B1 H8 N16384, bf16
-    q256, k256, v256 = (t.cuda() for t in make_inputs(B, H, N, 256, "bf16", 9, 1.0))
+    # head dimension 256 (one wave per SIMD) at B1 H8 N16384, bf16
+    q256, k256, v256, do256 = (t.cuda() for t in make_inputs(B, H, N, 256, "bf16", 9, 1.0, backward=True))
     o256 = torch.empty_like(q256)
+    g256 = tuple(torch.empty_like(q256) for _ in range(3))
+    ws256 = torch.empty(fa.bwd_workspace_bytes(B, H, N, 256), dtype=torch.uint8, device="cuda")
     t_f256 = _graph_ms(lambda: fa.fwd(q256, k256, v256, out=o256, lse=lse), 3)
+    t_b256 = _graph_ms(lambda: fa.bwd(q256, k256, v256, o256, lse, do256, workspace=ws256, out=g256), 2)
     fl_256 = 4 * B * H * N * N * 256
-    res["d256_fwd_B1H8N16384"] = {
+    res["d256_B1H8N16384"] = {
         "fwd_ms": round(t_f256, 5), "fwd_tflops": round(fl_256 / (t_f256 * 1e-3) / 1e12, 1),
-        "fwd_frac_peak": round(fl_256 / (t_f256 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    del q256, k256, v256, o256
+        "fwd_frac_peak": round(fl_256 / (t_f256 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "bwd_ms": round(t_b256, 5), "bwd_tflops": round(2.5 * fl_256 / (t_b256 * 1e-3) / 1e12, 1),
+        "bwd_frac_peak": round(2.5 * fl_256 / (t_b256 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q256, k256, v256, do256, o256, g256, ws256
     # dropout p = 0.1 at the benchmark shape (fa_fwd_dropout, fa_bwd_dropout)
     t_fd = _graph_ms(lambda: fa.fwd_dropout(q, k, v, 0.1, 1234, out=o, lse=lse), 3)
     t_bd = _graph_ms(lambda: fa.bwd_dropout(q, k, v, o, lse, dob, 0.1, 1234, workspace=ws16, out=grads), 3)

@@ -37,7 +37,7 @@ def test_fp16_forward(gpu_lib, N, d, causal):
 
 
 @pytest.mark.parametrize("N", [33, 300, 1000])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp16_backward(gpu_lib, N, d, causal):
     q, k, v, do = make_inputs(1, 2, N, d, "fp16", seed=1100 + N + d, backward=True)
