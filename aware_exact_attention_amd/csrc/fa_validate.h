@@ -284,7 +284,7 @@ inline const char* status_string(int st) {
     case kOk: return "FA_OK: success";
     case kErrNull: return "FA_ERR_NULL: a required pointer is NULL";
     case kErrShape: return "FA_ERR_SHAPE: B, H and N must be >= 1, each tensor < 2^31 elements and (N+256)*d*4 < 2^31";
-    case kErrHeadDim: return "FA_ERR_HEAD_DIM: head dimension d must be 64, 96 or 128 (or 256, forward only)";
+    case kErrHeadDim: return "FA_ERR_HEAD_DIM: head dimension d must be 64, 96 or 128 (or 256 on the forward and plain backward entry points)";
     case kErrScale: return "FA_ERR_SCALE: scale must be finite and > 0";
     case kErrAlign: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
     case kErrWorkspace: return "FA_ERR_WORKSPACE: workspace missing or smaller than the *_workspace_bytes() size";
