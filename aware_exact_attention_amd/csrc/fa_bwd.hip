@@ -146,17 +146,27 @@ struct DkdvTile {
   static constexpr int LDS = 2 * STAGE;        // double-buffered
   static constexpr int LPW = QT / 1024 / NW;   // 1 KiB direct loads per wave per Q (or dO) tile
   static_assert(QT % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
-  // MFMA slots of one step: S, dP over block 0 and block 1 (2*M), then
-  // dV, dK over block 0's and block 1's queries (2*M); H per product and block
+  // dK and dV columns are split over OS workgroups per key block at d = 256,
+  // each forming S and dP over the full d but accumulating DBO of the DB
+  // 32-column blocks: the accumulators of all 256 columns and the K and V
+  // fragments would not fit in a wave's 512 registers
+  static constexpr int OS = D == 256 ? 2 : 1;
+  static constexpr int DBO = DB / OS;
+  // MFMA slots of one step: S, dP over block 0 and block 1 (2*M; H per
+  // product and block), then dV, dK over block 0's and block 1's queries
+  // (2*M2; H2 per product and block)
   static constexpr int M = D / 8;
   static constexpr int H = M / 2;
+  static constexpr int H2 = 2 * DBO;
+  static constexpr int M2 = 2 * H2;
+  static constexpr int SLOTS = 2 * M + 2 * M2;
   static constexpr int PF = 3;                 // operand reads in flight
   static constexpr int PP = (8 + H - 1) / H;   // element pairs of VALU work per slot (8 pairs per block)
   // first slots of: P of block 0, dS of block 0, P of block 1, dS of block 1
   static constexpr int P0 = H + 2, D0 = 2 * H + 1, P1 = 3 * H + 2, D1 = 4 * H + 1;
 };
 
-// One workgroup of the dK/dV pass: key block `bid` of `nblk` (before the XCD
+// One workgroup of the dK/dV pass: workgroup `bid` of `nblk` (key block, before the XCD
 // remap).  smem holds DkdvTile<D>::LDS bytes; slist and scount are the
 // workgroup's query-step list (block-sparse mode only).
 template <typename E, int D, bool CAUSAL, bool DROP, int MODE>
@@ -177,13 +187,17 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses for the direct loads
   const int half = lane >> 5;
   const int l32 = lane & 31;
+  // the OS column parts of the grid are consecutive copies of the key-block grid
+  const int nper = nblk / T::OS;
+  const int cpart = T::OS == 1 ? 0 : bid / nper;
+  bid -= cpart * nper;
   int bh, jt;
   if (CAUSAL) {
     // key block jt sees the query steps from its diagonal on: block 0 has the
     // most, so the blocks go out longest first across all heads
-    causal_order(bid, nblk / Tk, Tk, bh, jt);
+    causal_order(bid, nper / Tk, Tk, bh, jt);
   } else {
-    const int tile = xcd_remap(bid, nblk);
+    const int tile = xcd_remap(bid, nper);
     bh = tile / Tk;
     jt = tile - bh * Tk;
   }
@@ -241,16 +255,16 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   int rof[T::KS];
 #pragma unroll
   for (int st = 0; st < T::KS; ++st) rof[st] = l32 * T::RS + (((2 * st + half) ^ tile_swz<D>(l32)) * 16);
-  int tof[T::DB][2];
+  int tof[T::DBO][2];
 #pragma unroll
-  for (int b = 0; b < T::DB; ++b) {
-    tof[b][0] = tr_off<D>(b, 0, lane);
-    tof[b][1] = tr_off<D>(b, 1, lane);
+  for (int b = 0; b < T::DBO; ++b) {
+    tof[b][0] = tr_off<D>(cpart * T::DBO + b, 0, lane);
+    tof[b][1] = tr_off<D>(cpart * T::DBO + b, 1, lane);
   }
 
-  f32x16 accv[T::DB], acck[T::DB];  // dV^T and dK^T of this wave's keys
+  f32x16 accv[T::DBO], acck[T::DBO];  // dV^T and dK^T of this wave's keys (this part's columns)
 #pragma unroll
-  for (int b = 0; b < T::DB; ++b) accv[b] = acck[b] = f32x16{};
+  for (int b = 0; b < T::DBO; ++b) accv[b] = acck[b] = f32x16{};
 
   const int Tq = (N + T::BQ - 1) / T::BQ;
   // this workgroup's query steps: [i0, i1), or (block-sparse) the steps
@@ -319,8 +333,9 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
         constexpr int qb = u / M, st = u % H, is_dp = (u % M) / H;
         return *reinterpret_cast<const v8*>(sb + (is_dp ? T::OFF_DO : 0) + qb * 32 * T::RS + rof[st]);
       } else {
-        constexpr int blk = (u - 2 * M) / M, is_dk = (u % M) / H, x = u % H;
-        constexpr int ps = 2 * blk + x / T::DB, b = x % T::DB;
+        constexpr int v = u - 2 * M, M2 = T::M2, H2 = T::H2;
+        constexpr int blk = v / M2, is_dk = (v % M2) / H2, x = v % H2;
+        constexpr int ps = 2 * blk + x / T::DBO, b = x % T::DBO;
         return tr_pair<E>(sb + (is_dk ? 0 : T::OFF_DO) + ps * 16 * T::RS, tof[b][0], tof[b][1]);
       }
     };
@@ -365,7 +380,7 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     };
 
     static_for<PF>([&](auto uc) { ring[decltype(uc)::value] = fetch(uc); });
-    static_for<4 * M>([&](auto uc) {
+    static_for<T::SLOTS>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
       const v8 a = ring[u % PF];
       if constexpr (u < 2 * M) {
@@ -373,12 +388,13 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
         if constexpr (!is_dp) s[qb] = mfma32(a, kf[st], st == 0 ? f32x16{} : s[qb]);
         else pd[qb] = mfma32(a, vf[st], st == 0 ? f32x16{} : pd[qb]);
       } else {
-        constexpr int blk = (u - 2 * M) / M, is_dk = (u % M) / H, x = u % H;
-        constexpr int ps = 2 * blk + x / T::DB, b = x % T::DB;
+        constexpr int v = u - 2 * M, M2 = T::M2, H2 = T::H2;
+        constexpr int blk = v / M2, is_dk = (v % M2) / H2, x = v % H2;
+        constexpr int ps = 2 * blk + x / T::DBO, b = x % T::DBO;
         if constexpr (!is_dk) accv[b] = mfma32(a, op[ps], accv[b]);
         else acck[b] = mfma32(a, os[ps], acck[b]);
       }
-      if constexpr (u + PF < 4 * M) ring[u % PF] = fetch(std::integral_constant<int, u + PF>{});
+      if constexpr (u + PF < T::SLOTS) ring[u % PF] = fetch(std::integral_constant<int, u + PF>{});
       // masks: S = -inf (P = 0) where the key is after the query (causal),
       // outside the query's window, or in a dropped block, on the steps that
       // need it only (a wave-uniform branch)
@@ -428,16 +444,17 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   const __amdgpu_buffer_rsrc_t rvo = make_rsrc(dV + head, head_bytes);
   const __amdgpu_buffer_rsrc_t rko = make_rsrc(dK + head, head_bytes);
 #pragma unroll
-  for (int b = 0; b < T::DB; ++b)
+  for (int b = 0; b < T::DBO; ++b)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      const int col = (cpart * T::DBO + b) * 32 + 8 * g + 4 * half;
       u32x2 w;
       w[0] = pack2<E>(accv[b][4 * g + 0] * fv, accv[b][4 * g + 1] * fv);
       w[1] = pack2<E>(accv[b][4 * g + 2] * fv, accv[b][4 * g + 3] * fv);
-      __builtin_amdgcn_raw_buffer_store_b64(w, rvo, key * T::GRS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, rvo, key * T::GRS + col * 2, 0, 0);
       w[0] = pack2<E>(acck[b][4 * g + 0] * scale, acck[b][4 * g + 1] * scale);
       w[1] = pack2<E>(acck[b][4 * g + 2] * scale, acck[b][4 * g + 3] * scale);
-      __builtin_amdgcn_raw_buffer_store_b64(w, rko, key * T::GRS + (b * 32 + 8 * g + 4 * half) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, rko, key * T::GRS + col * 2, 0, 0);
     }
 }
 
@@ -808,7 +825,7 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   if (e != hipSuccess) return e;
 
   const int Tk = (N + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV;
-  const long long Gk = (long long)B * H * Tk;
+  const long long Gk = (long long)B * H * Tk * DkdvTile<D>::OS;
   // dQ pass: eight waves (256 rows) per workgroup for d = 128 and 96 grids that cover
   // every CU (each K/V tile streamed once for twice the rows); four waves
   // otherwise.  Unlike the forward, the causal dQ pass gains from eight waves
@@ -913,7 +930,7 @@ static hipError_t launch_bwd_masked_t(const void* q, const void* k, const void* 
   if (e != hipSuccess) return e;
   const int Tk = (N + DkdvTile<D>::BKV - 1) / DkdvTile<D>::BKV;
   const int Tr = (N + DqTile<D, 4>::BR - 1) / DqTile<D, 4>::BR;
-  const long long Gk = (long long)B * H * Tk, Gq = (long long)B * H * Tr;
+  const long long Gk = (long long)B * H * Tk * DkdvTile<D>::OS, Gq = (long long)B * H * Tr;
   if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, false, MODE>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, (const E*)dO, (const float*)lse2, (const float*)Dv,
