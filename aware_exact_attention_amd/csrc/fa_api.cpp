@@ -107,7 +107,7 @@ int fa_bwd_fp16(const void* q, const void* k, const void* v, const void* o, cons
                 void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
                 size_t workspace_bytes, hipStream_t stream) {
   const fa::Shape s{B, H, N, d};
-  int st = fa::validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, workspace, workspace_bytes, true);
+  int st = fa::validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, workspace, workspace_bytes);
   if (st != fa::kOk) return st;
   st = fa::check_device();
   if (st != fa::kOk) return st;
@@ -178,7 +178,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, void* workspace,
            size_t workspace_bytes, hipStream_t stream) {
   const fa::Shape s{B, H, N, d};
-  int st = fa::validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, workspace, workspace_bytes, true);
+  int st = fa::validate_bwd(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal, workspace, workspace_bytes);
   if (st != fa::kOk) return st;
   st = fa::check_device();
   if (st != fa::kOk) return st;

@@ -891,6 +891,9 @@ static hipError_t launch_bwd_dropout_e(const void* q, const void* k, const void*
                                         float scale, int causal, float p, unsigned long long seed, void* ws,
                                         hipStream_t st) {
   const DropArgs dp = make_drop_args(p, seed);
+  if (d == 256)
+    return causal ? launch_bwd_t<E, 256, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
+                  : launch_bwd_t<E, 256, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
   if (d == 96)
     return causal ? launch_bwd_t<E, 96, true, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp)
                   : launch_bwd_t<E, 96, false, true>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, ws, st, dp);
@@ -949,6 +952,8 @@ static hipError_t launch_bwd_window_e(const void* q, const void* k, const void* 
                                       float scale, int left, int right, void* ws, hipStream_t st) {
   // a bound of N - 1 or more limits nothing: the same as no bound
   const MaskArgs mk{left >= N - 1 ? -1 : left, right >= N - 1 ? -1 : right, nullptr, 0, 0, H};
+  if (d == 256)
+    return launch_bwd_masked_t<E, 256, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
   if (d == 96)
     return launch_bwd_masked_t<E, 96, false, kMaskWindow>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk, ws, st);
   if (d == 128)
@@ -963,6 +968,11 @@ static hipError_t launch_bwd_blocksparse_e(const void* q, const void* k, const v
                                            int per_head, void* ws, hipStream_t st) {
   const int nb = (N + kMaskBlock - 1) / kMaskBlock;
   const MaskArgs mk{-1, -1, bm, per_head ? (long long)nb * nb : 0, nb, H};
+  if (d == 256)
+    return causal ? launch_bwd_masked_t<E, 256, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
+                                                                  ws, st)
+                  : launch_bwd_masked_t<E, 256, false, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale,
+                                                                   mk, ws, st);
   if (d == 96)
     return causal ? launch_bwd_masked_t<E, 96, true, kMaskBlocks>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, mk,
                                                                  ws, st)

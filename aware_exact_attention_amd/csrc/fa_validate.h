@@ -35,13 +35,12 @@ inline int64_t tensor_elems(const Shape& s) {
   return n;
 }
 
-// Head dimensions: 64, 96 and 128 everywhere; 256 on the forward entry points
-// and the plain backward (fa_bwd, fa_bwd_fp16): allow256.
-inline bool head_dim_ok(int d, bool allow256) { return d == 64 || d == 96 || d == 128 || (allow256 && d == 256); }
+// Head dimensions: 64, 96, 128 and 256 on every entry point.
+inline bool head_dim_ok(int d) { return d == 64 || d == 96 || d == 128 || d == 256; }
 
-inline int check_common(const Shape& s, float scale, int causal, bool allow256 = false) {
+inline int check_common(const Shape& s, float scale, int causal) {
   if (tensor_elems(s) < 0) return kErrShape;
-  if (!head_dim_ok(s.d, allow256)) return kErrHeadDim;
+  if (!head_dim_ok(s.d)) return kErrHeadDim;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return kErrScale;
   if (causal != 0 && causal != 1) return kErrArg;
   return kOk;
@@ -57,7 +56,7 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 inline int validate_fwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
                         const Shape& s, float scale, int causal, size_t elem_bytes) {
   if (!q || !k || !v || !o || !lse) return kErrNull;
-  int st = check_common(s, scale, causal, true);
+  int st = check_common(s, scale, causal);
   if (st != kOk) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return kErrAlign;
   const size_t tb = size_t(tensor_elems(s)) * elem_bytes;
@@ -79,7 +78,7 @@ struct BwdWorkspace {
 
 inline BwdWorkspace bwd_workspace_layout(const Shape& s) {
   const int64_t n = tensor_elems(s);
-  if (n < 0 || !head_dim_ok(s.d, true)) return BwdWorkspace{0, 0, 0};
+  if (n < 0 || !head_dim_ok(s.d)) return BwdWorkspace{0, 0, 0};
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t rows = size_t(s.B) * s.H * s.N;
   BwdWorkspace w;
@@ -94,9 +93,9 @@ inline size_t bwd_workspace_bytes(const Shape& s) { return bwd_workspace_layout(
 inline int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
                         const void* dO, const void* dq, const void* dk, const void* dv,
                         const Shape& s, float scale, int causal,
-                        const void* ws, size_t ws_bytes, bool allow256 = false) {
+                        const void* ws, size_t ws_bytes) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return kErrNull;
-  int st = check_common(s, scale, causal, allow256);
+  int st = check_common(s, scale, causal);
   if (st != kOk) return st;
   const void* all[9] = {q, k, v, o, lse, dO, dq, dk, dv};
   for (const void* p : all)
@@ -136,7 +135,7 @@ constexpr int kMaxMergeParts = 4096;
 // Number of key parts fa_fwd_splitkv uses for `requested` (<= 0: automatic),
 // or 0 if the shape is invalid.  Parts that would hold no tile are dropped.
 inline int split_count(const Shape& s, int requested) {
-  if (tensor_elems(s) < 0 || !head_dim_ok(s.d, true)) return 0;
+  if (tensor_elems(s) < 0 || !head_dim_ok(s.d)) return 0;
   const int tc = (s.N + kSplitKeyTile - 1) / kSplitKeyTile;
   long long S;
   if (requested > 0) {
@@ -203,7 +202,7 @@ inline int validate_lse_merge(const void* o_parts, const void* lse_parts, int S,
                               const Shape& s) {
   if (!o_parts || !lse_parts || !o || !lse) return kErrNull;
   if (tensor_elems(s) < 0) return kErrShape;
-  if (!head_dim_ok(s.d, true)) return kErrHeadDim;
+  if (!head_dim_ok(s.d)) return kErrHeadDim;
   if (S < 1 || S > kMaxMergeParts) return kErrArg;
   if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse)) return kErrAlign;
   const size_t rows = size_t(s.B) * s.H * s.N;
@@ -236,7 +235,7 @@ inline int validate_fwd_blocksparse(const void* q, const void* k, const void* v,
                                     const Shape& s, float scale, int causal, const void* block_mask,
                                     int per_head) {
   if (!block_mask || !q || !k || !v || !o || !lse) return kErrNull;
-  int st = check_common(s, scale, causal, true);
+  int st = check_common(s, scale, causal);
   if (st != kOk) return st;
   if (s.N > kMaxBlockSparseN) return kErrShape;
   if (per_head != 0 && per_head != 1) return kErrArg;
@@ -284,7 +283,7 @@ inline const char* status_string(int st) {
     case kOk: return "FA_OK: success";
     case kErrNull: return "FA_ERR_NULL: a required pointer is NULL";
     case kErrShape: return "FA_ERR_SHAPE: B, H and N must be >= 1, each tensor < 2^31 elements and (N+256)*d*4 < 2^31";
-    case kErrHeadDim: return "FA_ERR_HEAD_DIM: head dimension d must be 64, 96 or 128 (or 256 on the forward and plain backward entry points)";
+    case kErrHeadDim: return "FA_ERR_HEAD_DIM: head dimension d must be 64, 96, 128 or 256";
     case kErrScale: return "FA_ERR_SCALE: scale must be finite and > 0";
     case kErrAlign: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
     case kErrWorkspace: return "FA_ERR_WORKSPACE: workspace missing or smaller than the *_workspace_bytes() size";

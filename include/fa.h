@@ -24,9 +24,7 @@
  *   workspace included).  The library allocates no device memory, keeps no
  *   mutable global state, never synchronises and never prints; calls are
  *   re-entrant and thread-safe.
- * Preconditions: B, H, N >= 1; d in {64, 96, 128} (the forward entry points,
- *   fa_fwd*, fa_lse_merge, fa_bwd and fa_bwd_fp16 also take d = 256);
- *   causal in {0, 1};
+ * Preconditions: B, H, N >= 1; d in {64, 96, 128, 256}; causal in {0, 1};
  *   scale finite and > 0; B*H*N*d < 2^31 elements per tensor and
  *   (N + 256)*d*4 < 2^31 (one head's fp32 slab is addressed with 32-bit
  *   byte offsets).
@@ -55,7 +53,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,     /* B, H or N < 1, or a tensor or head too large for 32-bit offsets */
-  FA_ERR_HEAD_DIM = -3,  /* d is not 64, 96 or 128 (or 256 where the entry point takes it) */
+  FA_ERR_HEAD_DIM = -3,  /* d is not 64, 96, 128 or 256 */
   FA_ERR_SCALE = -4,     /* scale not finite or not > 0 */
   FA_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = -6, /* workspace missing or smaller than the matching *_workspace_bytes() */

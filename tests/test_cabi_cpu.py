@@ -135,7 +135,7 @@ def test_bwd_validation(lib, fn):
     assert call(dk=None) == ST["NULL"]
     assert call(N=0) == ST["SHAPE"]
     assert call(d=32) == ST["HEAD_DIM"]
-    assert call(d=512) == ST["HEAD_DIM"]  # d = 256 is accepted here (forward entry points and the plain backward)
+    assert call(d=512) == ST["HEAD_DIM"]  # d = 256 is accepted (every entry point)
     assert call(scale=float("nan")) == ST["SCALE"]
     assert call(causal=-1) == ST["ARG"]
     assert call(ws=None) == ST["WORKSPACE"]
@@ -330,15 +330,13 @@ int main() {
                                   0.125f, 1, mem[9], 3, ws, sizeof ws) == kErrArg);
   EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], Shape{1, 1, 8, 256}, 0.125f, 0, 2) == kOk);
   EXPECT(validate_fwd(mem[0], mem[1], mem[2], mem[3], mem[4], Shape{1, 1, 8, 96}, 0.125f, 0, 2) == kOk);
-  // d = 256: the plain backward only (allow256); the dropout and mask backwards keep the default
+  // d = 256 on every backward entry point; 512 nowhere
   EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], Shape{1, 1, 8, 256},
-                      0.125f, 1, ws, sizeof ws) == kErrHeadDim);
-  EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], Shape{1, 1, 8, 256},
-                      0.125f, 1, ws, sizeof ws, true) == kOk);
+                      0.125f, 1, ws, sizeof ws) == kOk);
   EXPECT(validate_bwd(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], Shape{1, 1, 8, 512},
-                      0.125f, 1, ws, sizeof ws, true) == kErrHeadDim);
+                      0.125f, 1, ws, sizeof ws) == kErrHeadDim);
   EXPECT(validate_bwd_window(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8],
-                             Shape{1, 1, 8, 256}, 0.125f, ws, sizeof ws) == kErrHeadDim);
+                             Shape{1, 1, 8, 256}, 0.125f, ws, sizeof ws) == kOk);
   EXPECT(bwd_workspace_bytes(Shape{1, 1, 8, 256}) == 512 && bwd_workspace_bytes(Shape{1, 1, 8, 96}) == 512);
   EXPECT(bwd_workspace_bytes(Shape{1, 1, 8, 512}) == 0);
   EXPECT(split_count(Shape{1, 1, 256, 256}, 2) == 2);

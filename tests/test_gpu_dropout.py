@@ -46,7 +46,7 @@ def test_dropout_p0_equals_plain(gpu_lib, causal):
 
 
 @pytest.mark.parametrize("N", [33, 300, 1000])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("p", [0.1, 0.3])
 def test_dropout_backward(gpu_lib, N, d, causal, p):

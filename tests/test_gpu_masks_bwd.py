@@ -49,7 +49,7 @@ def _window_case(fa, q, k, v, do, left, right, scale):
 
 
 @pytest.mark.parametrize("N", [1, 100, 300, 1000])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("window", WINDOWS, ids=[f"{a}_{b}" for a, b in WINDOWS])
 def test_window_bwd_small(gpu_lib, N, d, window):
     left, right = window
@@ -82,7 +82,7 @@ def _check_blocks(tag, got, ref, bm, causal, N):
 
 
 @pytest.mark.parametrize("N", [64, 130, 1000])
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("per_head", [False, True])
 def test_blocksparse_bwd_small(gpu_lib, N, d, causal, per_head):
