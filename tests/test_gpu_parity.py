@@ -305,7 +305,9 @@ def test_bwd_each_launch_shape(gpu_lib, H, N, d, causal):
     """The backward runs its two passes in one grid when both fit on the 256
     CUs together (128-key and 128-query blocks: B1 H2 N300 with 6 + 6
     workgroups, B1 H64 N256 with exactly 128 + 128) and as two launches
-    otherwise (B1 H128 N200: 256 + 256).  Each shape is compared in full."""
+    otherwise (B1 H128 N200: 256 + 256).  At d = 256 the dK/dV pass has two
+    workgroups per key block, so B1 H64 N256 (256 + 128) runs as two launches
+    there.  Each shape is compared in full."""
     q, k, v, do = make_inputs(1, H, N, d, "bf16", seed=900 + H + N + d, backward=True)
     scale = d ** -0.5
     _, _, dq, dk, dv = _bwd_case(gpu_lib, q, k, v, do, causal, scale)
