@@ -781,27 +781,27 @@ bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restr
 }
 
 // Both passes in one grid, for problems whose two grids together fit on the
-// CUs at once (B*H*ceil(N/128) <= 128 at four-wave dQ blocks): workgroups
-// [0, Gk) run the dK/dV pass, the rest the dQ pass, so neither pass leaves
-// half of the CUs idle while the other waits for it.  The passes share
-// nothing but their inputs.
-template <typename E, int D, bool CAUSAL, bool DROP>
+// CUs at once (Gk + Gq <= 256 workgroups; dense, window and block-sparse
+// alike): workgroups [0, Gk) run the dK/dV pass, the rest the dQ pass, so
+// neither pass leaves half of the CUs idle while the other waits for it.
+// The passes share nothing but their inputs.
+template <typename E, int D, bool CAUSAL, bool DROP, int MODE>
 __global__ void __launch_bounds__(256, 1)
 bwd_both_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
                 const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
                 E* __restrict__ dQ, E* __restrict__ dK, E* __restrict__ dV, DropArgs dp, int N, int Tk, int Tr,
-                int Gk, float c, float scale) {
+                int Gk, float c, float scale, MaskArgs mk) {
   constexpr int kLds = DkdvTile<D>::LDS > 2 * DqTile<D, 4>::STAGE ? DkdvTile<D>::LDS : 2 * DqTile<D, 4>::STAGE;
   __shared__ __attribute__((aligned(1024))) char smem[kLds];
-  __shared__ unsigned short list[1];
+  __shared__ unsigned short list[MODE == kMaskBlocks ? kMaxMaskTiles : 1];
   __shared__ int count;
   const int bid = blockIdx.x;
   if (bid < Gk)
-    dkdv_block<E, D, CAUSAL, DROP, kMaskDense>(Q, K, V, dO, LSE2, Dv, dK, dV, dp, N, Tk, c, scale, MaskArgs{}, bid,
-                                               Gk, smem, list, count);
+    dkdv_block<E, D, CAUSAL, DROP, MODE>(Q, K, V, dO, LSE2, Dv, dK, dV, dp, N, Tk, c, scale, mk, bid, Gk, smem, list,
+                                         count);
   else
-    dq_block<E, D, CAUSAL, 4, DROP, kMaskDense>(Q, K, V, dO, LSE2, Dv, dQ, dp, N, Tr, c, scale, MaskArgs{},
-                                                bid - Gk, (int)gridDim.x - Gk, smem, list, count);
+    dq_block<E, D, CAUSAL, 4, DROP, MODE>(Q, K, V, dO, LSE2, Dv, dQ, dp, N, Tr, c, scale, mk, bid - Gk,
+                                          (int)gridDim.x - Gk, smem, list, count);
 }
 
 // ---------------------------------------------------------------------------
@@ -838,9 +838,9 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   // Grids that fit on the CUs together run as one launch (1.5-1.7x faster at
   // B1 H8 N1024-2048 than two launches that each leave half of the CUs idle).
   if (!dq8 && Gk + Gq <= kNumCUs) {
-    hipLaunchKernelGGL((bwd_both_kernel<E, D, CAUSAL, DROP>), dim3((unsigned)(Gk + Gq)), dim3(256), 0, st,
+    hipLaunchKernelGGL((bwd_both_kernel<E, D, CAUSAL, DROP, kMaskDense>), dim3((unsigned)(Gk + Gq)), dim3(256), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)dO, (const float*)lse2, (const float*)Dv,
-                       (E*)dq, (E*)dk, (E*)dv, dp, N, Tk, Tr, (int)Gk, c, scale);
+                       (E*)dq, (E*)dk, (E*)dv, dp, N, Tk, Tr, (int)Gk, c, scale, MaskArgs{});
     return hipGetLastError();
   }
   hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, DROP, kMaskDense>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0,
@@ -935,6 +935,12 @@ static hipError_t launch_bwd_masked_t(const void* q, const void* k, const void* 
   const int Tr = (N + DqTile<D, 4>::BR - 1) / DqTile<D, 4>::BR;
   const long long Gk = (long long)B * H * Tk * DkdvTile<D>::OS, Gq = (long long)B * H * Tr;
   if (Gk > 0x7fffffffLL || Gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (Gk + Gq <= kNumCUs) {  // both passes in one launch, as in the dense backward
+    hipLaunchKernelGGL((bwd_both_kernel<E, D, CAUSAL, false, MODE>), dim3((unsigned)(Gk + Gq)), dim3(256), 0, st,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)dO, (const float*)lse2, (const float*)Dv,
+                       (E*)dq, (E*)dk, (E*)dv, DropArgs{}, N, Tk, Tr, (int)Gk, c, scale, mk);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, false, MODE>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, (const E*)dO, (const float*)lse2, (const float*)Dv,
                      (E*)dk, (E*)dv, DropArgs{}, N, Tk, c, scale, mk);

@@ -96,6 +96,24 @@ def test_blocksparse_bwd_small(gpu_lib, N, d, causal, per_head):
     _check_blocks(f"bwd blocksparse N={N} d={d} causal={causal} per_head={per_head}", got, ref, bm, causal, N)
 
 
+@pytest.mark.parametrize("H,N", [(2, 300), (128, 200)])
+@pytest.mark.parametrize("d", [128, 256])
+def test_masks_bwd_each_launch_shape(gpu_lib, H, N, d):
+    """The mask backwards run their two passes in one grid when both fit on
+    the 256 CUs together (B1 H2 N300) and as two launches otherwise (B1 H128
+    N200: 256 + 256 workgroups at d = 128).  Window (5, 3) and a random
+    per-head block mask with the causal limit, compared in full."""
+    q, k, v, do = make_inputs(1, H, N, d, "bf16", seed=1700 + H + N + d, backward=True)
+    scale = d ** -0.5
+    args64 = [to_f64(t) for t in (q, k, v, do)]
+    got = _window_case(gpu_lib, q, k, v, do, 5, 3, scale)
+    _check3(f"bwd window launch shape H={H} N={N} d={d}", got, oracle.ref_bwd_window(*args64, scale, 5, 3))
+    bm = _random_block_mask(H, (N + 63) // 64, 0.5, 1710 + H + N + d, True)
+    got = _blocks_case(gpu_lib, q, k, v, do, bm, True, scale)
+    ref = oracle.ref_bwd_blocksparse(*args64, scale, True, bm)
+    _check_blocks(f"bwd blocksparse launch shape H={H} N={N} d={d}", got, ref, bm, True, N)
+
+
 def test_blocksparse_bwd_all_ones_equals_dense(gpu_lib):
     """An all-ones mask visits the same steps and tiles in the same order as
     the dense backward, so the gradients agree bit for bit."""
