@@ -10,10 +10,12 @@
 //   D_i = sum_k dO_ik O_ik (= sum_j P_ij dP_ij),  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three kernels on the caller's stream, none of them with atomics:
+// Three kernels on the caller's stream, none of them with atomics (two when
+// the grids of passes 2 and 3 fit on the CUs together: bwd_both runs both):
 //  1. bwd_pre: D = rowsum(dO * O) and LSE in base-2 units, both fp32.
-//  2. bwd_dkdv: one workgroup per (b, h, 128-key block), four waves of 32
-//     keys, one wave per SIMD.  K and V of a wave's keys stay in registers as
+//  2. bwd_dkdv: one workgroup per (b, h, 128-key block) (two at d = 256,
+//     each with half of the dK and dV columns), four waves of 32 keys, one
+//     wave per SIMD.  K and V of a wave's keys stay in registers as
 //     the B operands of S = Q K^T and dP = dO V^T, so each lane holds one key
 //     and the recomputed P and dS feed dV^T += dO^T P and dK^T += Q^T dS
 //     straight from registers; dK^T and dV^T accumulate on chip for the whole
@@ -24,8 +26,8 @@
 //     dO^T are read with ds_read_b64_tr_b16.  Within a step the wave issues
 //     its MFMAs in a fixed order and spreads the exponentials and the dS
 //     arithmetic over the MFMAs that do not depend on them.
-//  3. bwd_dq: one workgroup per (b, h, 128-query block), laid out like the
-//     forward kernel: each wave owns 32 queries whose Q and dO fragments stay
+//  3. bwd_dq: one workgroup per (b, h, 128- or 256-query block), laid out
+//     like the forward kernel: each wave owns 32 queries whose Q and dO fragments stay
 //     in VGPRs, K and V tiles of 64 keys stream through double-buffered LDS,
 //     S^T = K Q^T and dP^T = V dO^T put one query per lane, and
 //     dQ^T += K^T dS^T takes dS^T from registers and K^T from transposing LDS
