@@ -97,7 +97,7 @@ def test_blocksparse_bwd_small(gpu_lib, N, d, causal, per_head):
 
 
 @pytest.mark.parametrize("H,N", [(2, 300), (128, 200)])
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 def test_masks_bwd_each_launch_shape(gpu_lib, H, N, d):
     """The mask backwards run their two passes in one grid when both fit on
     the 256 CUs together (B1 H2 N300) and as two launches otherwise (B1 H128

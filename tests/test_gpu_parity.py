@@ -9,13 +9,19 @@ Tolerances (written here, derived in the design notes):
 * O, bf16 path: max-abs <= 2e-2 and mean-abs <= 2e-3; fp32 path: max-abs <= 1e-5.
 * LSE: max-abs <= 1e-3 (bf16 path), <= 1e-5 (fp32 path).
 * dQ, dK, dV (bf16 path): max-abs <= 2e-2 * max|ref| and mean-abs <= 1e-2 * mean|ref|
-  (bf16 rounding of P, dS and of the outputs is 2^-9 relative each).
+  (bf16 rounding of P, dS, O and of the outputs is at most 2^-8 relative each;
+  the sums over keys and queries average the input roundings).  This replaces
+  the elementwise 2e-2 + 2^-8 |ref| rule first proposed for the gradients: it
+  is stricter for gradients of small magnitude, which the absolute 2e-2 term
+  would not test at all.
 
 Small sizes are compared element by element in full.  Full-size workloads are
 run in the same launch configuration the benchmark times and compared on
 sampled rows (forward: every head, rows at the start, the end, tile
-boundaries and random positions) or sampled heads (backward: all outputs of
-the sampled heads).
+boundaries and random positions) or in full (backward: every output of every
+head).  Gradients of inputs whose dS terms are much larger than the result
+(climbing scores) are held to an elementwise bound derived from the bf16
+roundings instead (``grad_error_bounds``).
 """
 from __future__ import annotations
 
@@ -159,6 +165,51 @@ def test_other_scale_and_peaked_rows(gpu_lib):
     check_lse("scale0.3_peaked", _np(lse), rl)
 
 
+def grad_error_bounds(q, k, v, do, scale, causal):
+    """Elementwise first-order bounds, in fp64 from the oracle's P, on what the
+    bf16 backward may differ from the exact gradients dQ and dK:
+
+    * dS is rounded to bf16 before the products dQ = scale dS K and
+      dK = scale dS^T Q: at most 2^-8 |dS_ij| each, so
+      scale 2^-8 (|dS| |K|) for dQ and scale 2^-8 (|dS|^T |Q|) for dK;
+    * D = rowsum(dO * O) is taken from the forward's bf16 O, whose error is at
+      most 2^-8 (P |V|) from P rounded for the P V product plus 2^-8 |O| from
+      its own rounding, together at most 2^-7 (P |V|); the resulting
+      |dD_i| <= 2^-7 sum_c |dO_ic| (P |V|)_ic enters dS_ij as P_ij dD_i, which
+      adds scale |dD| (P |K|) to dQ and scale P^T (|dD| |Q|) to dK.
+
+    The fp32 accumulations (relative 2^-24 per term) and the exponentials
+    (about 1 ulp) are orders of magnitude smaller.  The rounding of the result
+    to bf16 (2^-8 |dQ|) is added by the caller."""
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    P = oracle.ref_probs(q, k, scale, causal)
+    u = 2.0 ** -8
+    bq, bk = np.empty_like(q), np.empty_like(k)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            p = P[b, h]
+            dp = do[b, h] @ v[b, h].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dd = 2 * u * (np.abs(do[b, h]) * (p @ np.abs(v[b, h]))).sum(axis=1)
+            bq[b, h] = scale * (u * (np.abs(ds) @ np.abs(k[b, h])) + dd[:, None] * (p @ np.abs(k[b, h])))
+            bk[b, h] = scale * (u * (np.abs(ds).T @ np.abs(q[b, h])) + p.T @ (dd[:, None] * np.abs(q[b, h])))
+    return bq, bk
+
+
+# margin over the first-order bound for second-order terms and the ones it neglects
+BOUND_MARGIN = 1.25
+
+
+def check_grad_bound(name, what, got, ref, bound):
+    assert np.isfinite(got).all(), f"{name}: non-finite {what}"
+    err = np.abs(got - ref)
+    tol = BOUND_MARGIN * bound + 2.0 ** -8 * np.abs(ref) + 1e-6
+    worst = float((err / tol).max())
+    _report(check=name, what=what + "(bound)", max_abs=float(err.max()), ref_max=float(np.abs(ref).max()),
+            bound_max=float(bound.max()), worst_err_over_tol=worst)
+    assert worst <= 1.0, f"{name}: {what} error exceeds its rounding bound by {worst:.2f}x"
+
+
 @pytest.mark.parametrize("slope", [0.05, 0.3, 0.7, -0.4])
 @pytest.mark.parametrize("causal", [False, True])
 def test_climbing_scores(gpu_lib, slope, causal):
@@ -166,12 +217,12 @@ def test_climbing_scores(gpu_lib, slope, causal):
     in log2 units, plus small noise), so the running maximum of a row moves on
     every tile (slope 0.7: about 65 log2 units per 64-key tile), lags it by tens
     of log2 units for several tiles (0.3, 0.05), or never moves after the first
-    tile (negative slope).  The forward against the oracle, and dV of the
-    backward (which takes P from the forward's LSE).  dQ and dK are not compared
-    here: with a key component as large as 0.05 * j they sum dS terms about ten
-    times larger than the result, so the bf16 rounding of dS (2^-9 relative)
-    alone exceeds the relative tolerance.  That is the conditioning of these
-    inputs, not of the method; the other backward tests cover dQ and dK."""
+    tile (negative slope).  The forward against the oracle, and all three
+    gradients of the backward (which takes P from the forward's LSE).  With a key
+    component as large as 0.05 * j, dQ and dK sum dS terms up to ten times
+    larger than the result, so a bound relative to the result does not apply to
+    them; they are held to the bf16 rounding bound of ``grad_error_bounds``
+    instead, elementwise."""
     N, d = 1000, 64
     q, k, v, do = make_inputs(1, 2, N, d, "bf16", seed=310, backward=True)
     q = q * 0.05
@@ -185,12 +236,14 @@ def test_climbing_scores(gpu_lib, slope, causal):
     torch.cuda.synchronize()
     args = [to_f64(t) for t in (q, k, v, do)]
     ro, rl = oracle.ref_fwd(*args[:3], scale, causal)
-    _, _, rv = oracle.ref_bwd(*args, scale, causal)
+    rq, rk, rv = oracle.ref_bwd(*args, scale, causal)
     tag = f"climbing slope={slope} causal={causal}"
     check_o(tag, _np(o), ro)
     check_lse(tag, _np(lse), rl)
     check_grad(tag, "dV", _np(dv), rv)
-    assert torch.isfinite(dq).all().item() and torch.isfinite(dk).all().item()
+    bq, bk = grad_error_bounds(*args, scale, causal)
+    check_grad_bound(tag, "dQ", _np(dq), rq, bq)
+    check_grad_bound(tag, "dK", _np(dk), rk, bk)
 
 
 @pytest.mark.parametrize("name", ["gpt2", "gpt2_causal"])
@@ -299,7 +352,7 @@ def test_bwd_small(gpu_lib, N, d, causal):
 
 
 @pytest.mark.parametrize("H,N", [(2, 300), (64, 256), (128, 200)])
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_each_launch_shape(gpu_lib, H, N, d, causal):
     """The backward runs its two passes in one grid when both fit on the 256
@@ -318,27 +371,36 @@ def test_bwd_each_launch_shape(gpu_lib, H, N, d, causal):
     check_grad(tag, "dV", dv, rv)
 
 
+@pytest.mark.parametrize("d", [96, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_ragged_many_heads(gpu_lib, causal):
-    """256 heads of 300 rows: a grid large enough for the 256-row dQ
-    workgroups (non-causal, d = 128), with a ragged tail in every head."""
-    q, k, v, do = make_inputs(1, 256, 300, 128, "bf16", seed=450, backward=True)
-    scale = 128 ** -0.5
+def test_bwd_ragged_many_heads(gpu_lib, d, causal):
+    """256 heads of 300 rows: a grid large enough for the 256-row (eight-wave)
+    dQ workgroups at d = 96 and 128, with a ragged tail in every head."""
+    q, k, v, do = make_inputs(1, 256, 300, d, "bf16", seed=450 + d, backward=True)
+    scale = d ** -0.5
     _, _, dq, dk, dv = _bwd_case(gpu_lib, q, k, v, do, causal, scale)
     rq, rk, rv = oracle.ref_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal)
-    tag = f"bwd many heads N=300 d=128 causal={causal}"
+    tag = f"bwd many heads N=300 d={d} causal={causal}"
     check_grad(tag, "dQ", dq, rq)
     check_grad(tag, "dK", dk, rk)
     check_grad(tag, "dV", dv, rv)
 
 
-@pytest.mark.parametrize("name,heads", [("fwd_bwd_causal", [(0, 0), (1, 7), (3, 15)]), ("bwd_16k", [(0, 5)])])
-def test_full_size_backward_sampled_heads(gpu_lib, name, heads):
+_FULL_BWD_CASES = [("fwd_bwd_causal", b) for b in range(4)] + [("bwd_16k", (0, 4)), ("bwd_16k", (4, 8))]
+
+
+@pytest.mark.parametrize("name,part", _FULL_BWD_CASES, ids=[f"{n}-{p}" for n, p in _FULL_BWD_CASES])
+def test_full_size_backward_every_head(gpu_lib, name, part):
+    """The full-size backward workloads in the launch configuration the
+    benchmark times, every head compared in full with the oracle: the
+    forward+backward workload B4 H16 N4096 causal one batch entry per case, the
+    benchmark workload B1 H8 N16384 four heads per case."""
     w = WORKLOADS[name]
     q, k, v, do = workload_inputs(w)
     o, lse, dq, dk, dv = _bwd_case(gpu_lib, q, k, v, do, w.causal, w.scale)
     for arr in (o, lse, dq, dk, dv):
         assert np.isfinite(arr).all()
+    heads = [(part, h) for h in range(w.H)] if name == "fwd_bwd_causal" else [(0, h) for h in range(*part)]
     for b, h in heads:
         sl = (slice(b, b + 1), slice(h, h + 1))
         args = [to_f64(t[sl]) for t in (q, k, v, do)]

@@ -7,14 +7,21 @@ attention, itself pinned in ``test_oracle.py``), by the keep rate, by central
 finite differences of the backward with the mask held fixed, and by
 torch.autograd on plain fp64 ops with the same mask.
 
+The full 10-round stream is pinned against an independent implementation:
+rocRAND's open-source Philox4x32-10 engine (``rocrand/rocrand_philox4x32_10.h``
+of the ROCm install, host-callable), compiled with g++ into a small host
+program and compared word for word on random (counter, key) pairs.
+
 What is a reading and not pinned by anything outside this build: the mapping of
-(b, h, i, j) to counters, words and bytes (a convention both sides implement),
-and the exact 10-round stream beyond the special cases (no published test
-vectors are available offline).
+(b, h, i, j) to counters, words and bytes (a convention both sides implement).
 """
 from __future__ import annotations
 
+import functools
 import math
+import os
+import subprocess
+import tempfile
 
 import numpy as np
 import pytest
@@ -132,8 +139,94 @@ def pin_autograd(R):
         np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-13)
 
 
-PINS = [pin_philox_one_round, pin_philox_key_schedule, pin_philox_statistics, pin_p_zero_is_plain,
-        pin_keep_rate, pin_finite_differences, pin_autograd]
+ROCRAND_HEADER = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
+# Host program around rocRAND's engine: reads "c0 c1 c2 c3 k0 k1" lines and
+# prints the four words of the 10-round block function.  The block function
+# is a protected member of the engine; a derived class exposes it.  The
+# engine's public seeding path (seed -> key, subsequence -> (c2, c3),
+# offset / 4 -> (c0, c1)) is printed beside it for the small counters where
+# that path can express the counter (4 * (c1:c0) < 2^64).
+_ROCRAND_PROBE = r"""
+#include <rocrand/rocrand_philox4x32_10.h>
+#include <cstdio>
+struct Probe : rocrand_device::philox4x32_10_engine {
+  uint4 block(uint4 c, uint2 k) { return ten_rounds(c, k); }
+};
+int main() {
+  unsigned c0, c1, c2, c3, k0, k1;
+  Probe p;
+  while (std::scanf("%u %u %u %u %u %u", &c0, &c1, &c2, &c3, &k0, &k1) == 6) {
+    uint4 c; c.x = c0; c.y = c1; c.z = c2; c.w = c3;
+    uint2 k; k.x = k0; k.y = k1;
+    const uint4 w = p.block(c, k);
+    unsigned e[4] = {0, 0, 0, 0};
+    if (c1 < (1u << 30)) {
+      rocrand_device::philox4x32_10_engine g((unsigned long long)k1 << 32 | k0,
+                                             (unsigned long long)c3 << 32 | c2,
+                                             4ull * ((unsigned long long)c1 << 32 | c0));
+      for (int i = 0; i < 4; ++i) e[i] = g();
+    }
+    std::printf("%u %u %u %u %u %u %u %u\n", w.x, w.y, w.z, w.w, e[0], e[1], e[2], e[3]);
+  }
+  return 0;
+}
+"""
+
+
+@functools.lru_cache(maxsize=1)
+def _rocrand_probe() -> str:
+    d = tempfile.mkdtemp(prefix="philox_rocrand_")
+    src, exe = os.path.join(d, "probe.cpp"), os.path.join(d, "probe")
+    with open(src, "w") as f:
+        f.write(_ROCRAND_PROBE)
+    subprocess.run(["g++", "-O1", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", src, "-o", exe],
+                   check=True, capture_output=True, text=True)
+    return exe
+
+
+def _rocrand_words(ctr: np.ndarray, key: np.ndarray):
+    """rocRAND's 10-round outputs for rows (c0, c1, c2, c3) and (k0, k1): block words, engine words."""
+    lines = "\n".join(" ".join(str(int(x)) for x in (*c, *k)) for c, k in zip(ctr, key)) + "\n"
+    out = subprocess.run([_rocrand_probe()], input=lines, capture_output=True, text=True, check=True).stdout
+    vals = np.array([[int(x) for x in ln.split()] for ln in out.strip().splitlines()], dtype=np.uint64)
+    return vals[:, :4], vals[:, 4:]
+
+
+def pin_philox_rocrand(R):
+    """Ten rounds against rocRAND's Philox4x32-10, word for word: 40 random keys
+    with 300 random counters each (full 32-bit range; a third of them small, as
+    the dropout mask uses, a third with c1 < 2^30 so that the engine's public
+    seeding path applies), plus the all-zero and all-ones cases."""
+    if not os.path.exists(ROCRAND_HEADER):
+        raise AssertionError(f"{ROCRAND_HEADER} missing: the 10-round pin cannot run")
+    rng = np.random.default_rng(20260101)
+    nk, nc = 40, 300
+    keys = rng.integers(0, 1 << 32, size=(nk, 2), dtype=np.uint64)
+    keys[0] = 0
+    keys[1] = 0xFFFFFFFF
+    ctr = rng.integers(0, 1 << 32, size=(nk, nc, 4), dtype=np.uint64)
+    ctr[:, : nc // 3, 1] &= (1 << 30) - 1
+    ctr[:, nc // 3: 2 * nc // 3, 1:] = 0
+    ctr[:, nc // 3: 2 * nc // 3, 0] &= 0xFFFF
+    ctr[0, 0] = 0
+    ctr[1, 0] = 0xFFFFFFFF
+    flat_c = ctr.reshape(-1, 4)
+    flat_k = np.repeat(keys, nc, axis=0)
+    block, engine = _rocrand_words(flat_c, flat_k)
+    got = np.empty_like(block)
+    for i in range(nk):
+        w = R.philox4x32(*(ctr[i, :, j] for j in range(4)), int(keys[i, 0]), int(keys[i, 1]))
+        got[i * nc:(i + 1) * nc] = np.stack([np.asarray(x, dtype=np.uint64) for x in w], axis=1)
+    bad = np.nonzero((got != block).any(axis=1))[0]
+    assert bad.size == 0, (f"{bad.size} of {len(flat_c)} blocks differ from rocRAND "
+                           f"(first: counter {flat_c[bad[0]]}, key {flat_k[bad[0]]})")
+    seeded = flat_c[:, 1] < (1 << 30)
+    assert seeded.sum() > nk * nc // 3
+    assert np.array_equal(engine[seeded], block[seeded]), "rocRAND's seeding path disagrees with its block function"
+
+
+PINS = [pin_philox_one_round, pin_philox_key_schedule, pin_philox_statistics, pin_philox_rocrand,
+        pin_p_zero_is_plain, pin_keep_rate, pin_finite_differences, pin_autograd]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -156,6 +249,16 @@ def _mut_philox_no_key_bump(c0, c1, c2, c3, k0, k1, rounds=10):
     for _ in range(rounds):
         out = _ORIG_PHILOX(*out, k0, k1, rounds=1)
     return out
+
+
+# A stream of 9 or 7 rounds whose round function is right: the one- and
+# two-round special cases still hold, so only the rocRAND pin sees it.
+def _mut_philox_9_rounds(c0, c1, c2, c3, k0, k1, rounds=10):
+    return _ORIG_PHILOX(c0, c1, c2, c3, k0, k1, 9 if rounds == 10 else rounds)
+
+
+def _mut_philox_7_rounds(c0, c1, c2, c3, k0, k1, rounds=10):
+    return _ORIG_PHILOX(c0, c1, c2, c3, k0, k1, 7 if rounds == 10 else rounds)
 
 
 def _mut_bwd_unmasked_dp(q, k, v, do, scale, causal, p, seed):
@@ -181,6 +284,8 @@ def _mut_no_rescale(p):
 MUTANTS = {
     "philox_words_swapped": ("philox4x32", _mut_philox_words_swapped),
     "philox_no_key_bump": ("philox4x32", _mut_philox_no_key_bump),
+    "philox_9_rounds": ("philox4x32", _mut_philox_9_rounds),
+    "philox_7_rounds": ("philox4x32", _mut_philox_7_rounds),
     "bwd_unmasked_dp": ("ref_bwd_dropout", _mut_bwd_unmasked_dp),
     "no_rescale_of_kept": ("dropout_scale", _mut_no_rescale),
 }
