@@ -44,6 +44,7 @@ hipError_t launch_bwd_blocksparse(const void* q, const void* k, const void* v, c
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                       int causal, void* ws, hipStream_t st);
+hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t st);
 
 namespace {
 // Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, 2 no.  Written
@@ -355,6 +356,15 @@ int fa_bwd_blocksparse_fp16(const void* q, const void* k, const void* v, const v
                             size_t workspace_bytes, hipStream_t stream) {
   return fa_bwd_blocksparse_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, block_mask,
                                  mask_per_head, workspace, workspace_bytes, stream, true);
+}
+
+int fa_probe_mfma_bf16(int workgroups, int iters, float* sink, hipStream_t stream) {
+  if (!sink) return fa::kErrNull;
+  if (workgroups < 1 || iters < 1 || workgroups > (1 << 20)) return fa::kErrArg;
+  if (!fa::aligned16(sink)) return fa::kErrAlign;
+  const int st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_mfma_probe(workgroups, iters, sink, stream) == hipSuccess ? fa::kOk : fa::kErrHip;
 }
 
 const char* fa_status_string(int status) { return fa::status_string(status); }

@@ -812,4 +812,36 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                 : launch_fwd_f32_t<64, false>(q, k, v, o, lse, B, H, N, scale, st);
 }
 
+// ---------------------------------------------------------------------------
+// Measurement helper: the bf16 MFMA rate this GPU sustains.  Each wave runs
+// `iters` rounds of four independent v_mfma_f32_32x32x16_bf16 accumulation
+// chains on register operands (no memory traffic in the loop), two waves per
+// SIMD, and writes one sum per wave so that nothing is optimised away.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256, 2) mfma_probe_kernel(int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(0.001f * float((lane + e) & 7));
+    b[e] = (__bf16)(0.001f * float((lane * 3 + e) & 7));
+  }
+  f32x16 acc[4] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = mfma32(a, b, acc[c]);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t += acc[c][e];
+  sink[size_t(blockIdx.x) * 256 + threadIdx.x] = t;
+}
+
+hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)workgroups), dim3(256), 0, st, iters, sink);
+  return hipGetLastError();
+}
+
 }  // namespace fa

@@ -30,6 +30,7 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "fa_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
                         _c_int, _vp, _c_size_t, _vp]),
+    "fa_probe_mfma_bf16": (_c_int, [_c_int, _c_int, _vp, _vp]),
     "fa_fwd_splitkv_parts": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "fa_fwd_splitkv_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "fa_fwd_splitkv": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int,
@@ -176,6 +177,16 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, w
     if st != 0:
         raise FAError(st, name)
     return dq, dk, dv
+
+
+def probe_mfma_bf16(workgroups: int, iters: int, sink: torch.Tensor) -> None:
+    """Enqueue the MFMA-rate probe (``fa_probe_mfma_bf16``); FLOP = workgroups*4*iters*4*32768."""
+    _check(sink, "sink", torch.float32)
+    if sink.numel() < workgroups * 256:
+        raise ValueError("sink needs workgroups*256 floats")
+    st = load().fa_probe_mfma_bf16(int(workgroups), int(iters), sink.data_ptr(), _stream())
+    if st != 0:
+        raise FAError(st, "fa_probe_mfma_bf16")
 
 
 def splitkv_parts(B: int, H: int, N: int, d: int, num_splits: int = 0) -> int:

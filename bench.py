@@ -8,8 +8,9 @@ deployment page, benchmark section).  Inputs are resident in HBM before the
 timed region.  The forward and backward calls are bracketed by HIP events on
 the stream they run on, so their per-call durations are measured live.
 
-Prints ONE JSON line.  `value` is the algorithmic TFLOP/s of the step
-(forward 4*B*H*N^2*d plus backward 10*B*H*N^2*d, divided by the step time).
+Prints ONE JSON line.  `value` is the forward's algorithmic TFLOP/s
+(4*B*H*N^2*d over the median HIP-event time of fa_fwd), the metric's first
+figure; the backward (10*B*H*N^2*d) and the whole step are reported beside it.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -67,6 +69,9 @@ def parse():
                    help="HBM bytes per launch measured with rocprofv3 counters (written by --traffic-from)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of COPY_BYTES (for the FETCH_SIZE / WRITE_SIZE calibration)")
+    p.add_argument("--trace-summary", metavar="TRACE_DIR",
+                   help="summarise a rocprofv3 --kernel-trace run of this benchmark (the last --steps dispatches "
+                        "of each kernel) as a markdown table, then exit")
     p.add_argument("--traffic-from", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output of the bench and of --copy-calibration "
                         "into the traffic summary, then exit")
@@ -125,14 +130,26 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES, "calls": 5}))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, q, k, v, do, heads: int):
-    """Time the fp64 oracle (as it stands) on `heads` heads of the workload on the host cores."""
+    """Time the fp64 oracle (as it stands) on `heads` heads of the workload on the host cores,
+    and single-threaded on the two smallest workloads (tiny fp32, one GPT-2-shaped head)."""
     import numpy as np  # noqa: F401
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         threads = len(os.sched_getaffinity(0))
     sl = (slice(0, 1), slice(0, heads))
     args = [to_f64(t[sl]) for t in (q, k, v, do)]
@@ -143,6 +160,23 @@ def cpu_baseline(w, q, k, v, do, heads: int):
     t2 = time.perf_counter()
     frac = heads / (w.B * w.H)
     flop = (w.fwd_flop + w.bwd_flop) * frac
+    single = {}
+    for name, nheads in (("tiny_f32", 1), ("gpt2", 1)):
+        wl = WORKLOADS[name]
+        ins = make_inputs(wl.B, wl.H, wl.N, wl.d, wl.dtype, wl.seed, wl.qk_std)
+        a = [to_f64(t[:1, :nheads]) for t in ins]
+        reps = 20 if name == "tiny_f32" else 3
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                s0 = time.perf_counter()
+                for _ in range(reps):
+                    oracle.ref_fwd(*a, wl.scale, wl.causal)
+                dt = (time.perf_counter() - s0) / reps
+        else:  # pragma: no cover
+            dt = float("nan")
+        fl = wl.fwd_flop * nheads / (wl.B * wl.H)
+        single[name] = {"s_per_head_fwd": round(dt, 6), "gflops": round(fl / dt / 1e9, 3), "threads": 1,
+                        "sample": f"ref_fwd on {nheads} of {wl.B * wl.H} heads, mean of {reps} calls"}
     return {
         "value": round(flop / (t2 - t0) / 1e12, 6),
         "unit": "TFLOP/s",
@@ -151,7 +185,70 @@ def cpu_baseline(w, q, k, v, do, heads: int):
         "sample": f"fp64 oracle ref_fwd + ref_bwd on {heads} of {w.B * w.H} heads of the benchmark workload "
                   f"(N={w.N}, d={w.d}); fwd {t1 - t0:.2f} s, bwd {t2 - t1:.2f} s; TFLOP/s of that sample",
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
+        "single_thread": single,
     }
+
+
+def mfma_ceiling():
+    """The bf16 MFMA rate the GPU sustains (fa_probe_mfma_bf16: four independent
+    chains per wave, two waves per SIMD, register operands), next to the spec."""
+    wgs, iters = 2048, 4000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    fa.probe_mfma_bf16(wgs, iters, sink)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fa.probe_mfma_bf16(wgs, iters, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = statistics.median(ts)
+    flop = wgs * 4 * iters * 4 * 32768
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"measured_tflops": round(tf, 1), "spec_tflops": PEAK_BF16_TFLOPS,
+            "frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4),
+            "clock_ghz_at_full_mfma_rate": round(tf * 1e12 / (256 * 4096) / 1e9, 3),
+            "probe": f"fa_probe_mfma_bf16: {wgs} workgroups x 4 waves x {iters} x 4 chains of "
+                     f"v_mfma_f32_32x32x16_bf16, median of 5 calls ({ms:.3f} ms)"}
+
+
+def trace_summary(trace_dir: str, steps: int):
+    """Markdown table of a rocprofv3 kernel trace of this benchmark: per kernel of the
+    step, mean and median duration over its last `steps` dispatches (the timed steps;
+    warm-up calls excluded) and the fraction of the bf16 peak at the algorithmic FLOP."""
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    w = WORKLOADS["bwd_16k"]
+    per = {}
+    for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
+        name = r["Kernel_Name"]
+        for n in FWD_KERNELS + BWD_KERNELS:
+            if n in name:
+                per.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| Kernel | Dispatches in trace | Mean of last %d (us) | Median of last %d (us) |" % (steps, steps),
+           "|---|---|---|---|"]
+    means = {}
+    for n in FWD_KERNELS + BWD_KERNELS:
+        ds = per.get(n, [])[-steps:]
+        if not ds:
+            continue
+        means[n] = (statistics.mean(ds), statistics.median(ds))
+        out.append(f"| `{n}` | {len(per[n])} | {means[n][0]:.1f} | {means[n][1]:.1f} |")
+    f_us = means.get("fwd_kernel", (float("nan"),) * 2)
+    b_us = [sum(means[n][i] for n in BWD_KERNELS if n in means) for i in (0, 1)]
+    out.append("")
+    for label, flop, us in (("forward (fwd_kernel)", w.fwd_flop, f_us),
+                            ("backward (sum of the three kernels)", w.bwd_flop, b_us)):
+        tf = [flop / (u * 1e-6) / 1e12 for u in us]
+        out.append(f"- {label}: mean {us[0]:.1f} us -> {tf[0]:.1f} TFLOP/s = {tf[0] / PEAK_BF16_TFLOPS:.4f} of "
+                   f"{PEAK_BF16_TFLOPS}; median {us[1]:.1f} us -> {tf[1]:.1f} TFLOP/s = "
+                   f"{tf[1] / PEAK_BF16_TFLOPS:.4f}")
+    print("\n".join(out))
 
 
 def _graph_ms(fn, calls: int, warmup: int = 3) -> float:
@@ -196,11 +293,21 @@ def config_rows():
         # the clock has settled after the host-side input generation
         calls = max(3, min(50, int(2e13 / max(w.fwd_flop, 1))))
         t_f = _graph_ms(lambda: fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse), calls)
+        # peak device memory of one call: the library allocates nothing, so it is the
+        # caller's q, k, v, o and lse (the pages' second benchmark column)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        peak_bytes = torch.cuda.max_memory_allocated()
+        extra = peak_bytes - base
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
         r = {"shape": [w.B, w.H, w.N, w.d], "dtype": w.dtype, "causal": w.causal,
              "peak_tflops": peak,
              "fwd_ms": round(t_f, 5), "fwd_tflops": round(w.fwd_flop / (t_f * 1e-3) / 1e12, 1),
-             "fwd_frac_peak": round(w.fwd_flop / (t_f * 1e-3) / 1e12 / peak, 4)}
+             "fwd_frac_peak": round(w.fwd_flop / (t_f * 1e-3) / 1e12 / peak, 4),
+             "peak_mem_gb": round(peak_bytes / 1e9, 4), "fwd_extra_alloc_bytes": int(extra)}
         if w.backward:
             do = ts[3].cuda()
             grads = tuple(torch.empty_like(q) for _ in range(3))
@@ -342,6 +449,9 @@ def next_rows():
 
 def main():
     a = parse()
+    if a.trace_summary:
+        trace_summary(a.trace_summary, a.steps)
+        return
     if a.traffic_from:
         traffic_from(*a.traffic_from, a.traffic_json)
         return
@@ -392,11 +502,16 @@ def main():
         assert torch.isfinite(t).all().item(), "non-finite output"
 
     ms_step = (t1 - t0) * 1e3 / a.steps
-    f_ms = sum(fwd_ms) / len(fwd_ms)
-    b_ms = sum(bwd_ms) / len(bwd_ms)
+
+    def stats(ms):
+        return {"ms_mean": round(statistics.mean(ms), 4), "ms_median": round(statistics.median(ms), 4),
+                "ms_min": round(min(ms), 4)}
+
+    f_ms = statistics.median(fwd_ms)
+    b_ms = statistics.median(bwd_ms)
     f_tf = w.fwd_flop / (f_ms * 1e-3) / 1e12
     b_tf = w.bwd_flop / (b_ms * 1e-3) / 1e12
-    value = (w.fwd_flop + w.bwd_flop) / (ms_step * 1e-3) / 1e12
+    step_tf = (w.fwd_flop + w.bwd_flop) / (ms_step * 1e-3) / 1e12
 
     # measured HBM bytes per launch, valid only for the kernel sources they were taken on
     traffic = {}
@@ -413,15 +528,16 @@ def main():
     # The backward call (2.5x the forward's algorithmic FLOPs) dominates the step.
     r_bwd = roof(w.bwd_flop, b_ms, "bwd")
     r_bwd["kernel"] = ("fa_bwd: bwd_pre_kernel + bwd_dkdv_kernel + bwd_dq_kernel (one HIP event pair around the "
-                       "call); FLOP = 10*B*H*N^2*d algorithmic (the dQ pass's recompute of S and dP not counted)")
+                       "call, median over the timed steps); FLOP = 10*B*H*N^2*d algorithmic (the dQ pass's "
+                       "recompute of S and dP not counted)")
     r_fwd = roof(w.fwd_flop, f_ms, "fwd")
-    r_fwd["kernel"] = "fa_fwd: fwd_kernel (bf16, 8 waves); FLOP = 4*B*H*N^2*d"
+    r_fwd["kernel"] = "fa_fwd: fwd_kernel (bf16, 8 waves; median over the timed steps); FLOP = 4*B*H*N^2*d"
     bytes_fwd = w.B * w.H * w.N * (8 * w.d + 4)
     bytes_bwd = w.B * w.H * w.N * (16 * w.d + 12)
 
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(f_tf, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
@@ -435,14 +551,18 @@ def main():
         "config": {"workload": f"attention fwd+bwd B{w.B} H{w.H} N{w.N} d{w.d} bf16 "
                                f"{'causal' if w.causal else 'non-causal'}, seeded N(0,1) inputs",
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed},
-        "fwd": {"ms": round(f_ms, 4), "tflops": round(f_tf, 2), "frac_peak": round(f_tf / PEAK_BF16_TFLOPS, 4),
-                "algorithmic_bytes": bytes_fwd,
+        "value_is": "forward TFLOP/s (4*B*H*N^2*d over the median event time of fa_fwd)",
+        "fwd": {"ms": round(f_ms, 4), **stats(fwd_ms), "tflops": round(f_tf, 2),
+                "frac_peak": round(f_tf / PEAK_BF16_TFLOPS, 4), "algorithmic_bytes": bytes_fwd,
                 "pages_a100_context": "pages: 28.5 ms (38.6 TFLOP/s derived) on an A100 at this shape, forward only"},
-        "bwd": {"ms": round(b_ms, 4), "tflops": round(b_tf, 2), "frac_peak": round(b_tf / PEAK_BF16_TFLOPS, 4),
-                "algorithmic_bytes": bytes_bwd},
+        "bwd": {"ms": round(b_ms, 4), **stats(bwd_ms), "tflops": round(b_tf, 2),
+                "frac_peak": round(b_tf / PEAK_BF16_TFLOPS, 4), "algorithmic_bytes": bytes_bwd},
+        "step": {"ms": round(ms_step, 4), "tflops": round(step_tf, 2),
+                 "note": "fa_fwd + fa_bwd per step, host wall clock around the timed steps"},
         "roofline": r_bwd,
         "roofline_fwd": r_fwd,
     }
+    out["mfma_ceiling"] = mfma_ceiling()
     if not a.no_next_rows:
         out["configs"] = config_rows()
         out["next_rows"] = next_rows()

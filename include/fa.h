@@ -315,6 +315,19 @@ int fa_bwd_dropout_fp16(const void* q, const void* k, const void* v, const void*
                         int causal, float dropout_p, unsigned long long seed, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fa_probe_mfma_bf16 - measurement helper, not part of the attention path:
+ * launches `workgroups` workgroups of four waves (two per SIMD), each wave
+ * running `iters` rounds of four independent bf16 32x32x16 MFMA accumulation
+ * chains on register operands, and writes one float per thread to `sink`
+ * (device, >= workgroups*256 floats, 16-byte aligned).  Timing it gives the
+ * dense bf16 MFMA rate the GPU sustains, to set beside the published peak:
+ * FLOP per call = workgroups * 4 * iters * 4 * 32768.  Errors: FA_ERR_NULL,
+ * FA_ERR_ARG (workgroups outside [1, 2^20] or iters < 1), FA_ERR_ALIGN,
+ * FA_ERR_DEVICE, FA_ERR_HIP.
+ */
+int fa_probe_mfma_bf16(int workgroups, int iters, float* sink, hipStream_t stream);
+
 /* fa_status_string - static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

@@ -37,7 +37,7 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_bytes", "fa_bwd",
+    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_bytes", "fa_bwd", "fa_probe_mfma_bf16",
                                            "fa_fwd_fp16", "fa_bwd_fp16", "fa_fwd_dropout", "fa_bwd_dropout",
                                            "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_bytes",
                                            "fa_fwd_splitkv", "fa_lse_merge", "fa_fwd_window",
@@ -144,6 +144,14 @@ def test_bwd_validation(lib, fn):
     assert call(dk=dq) == ST["ARG"]          # two outputs alias
     assert call(dv=v) == ST["ARG"]           # output aliases an input
     assert call(ws=dq) == ST["ARG"]          # workspace aliases an output
+
+
+def test_probe_validation(lib):
+    b = _Buf(4096)
+    assert lib.fa_probe_mfma_bf16(1, 1, None, None) == ST["NULL"]
+    assert lib.fa_probe_mfma_bf16(0, 1, b.ptr, None) == ST["ARG"]
+    assert lib.fa_probe_mfma_bf16(1, 0, b.ptr, None) == ST["ARG"]
+    assert lib.fa_probe_mfma_bf16(1, 1, b.ptr + 4, None) == ST["ALIGN"]
 
 
 def test_splitkv_parts_and_workspace(lib):
