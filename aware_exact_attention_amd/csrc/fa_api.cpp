@@ -45,6 +45,9 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
                       int causal, void* ws, hipStream_t st);
 hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t st);
+hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                              int causal, hipStream_t st);
 
 namespace {
 // Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, 2 no.  Written
@@ -185,6 +188,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (st != fa::kOk) return st;
   return fa::launch_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, workspace, stream) ==
                  hipSuccess
+             ? fa::kOk
+             : fa::kErrHip;
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                   hipStream_t stream) {
+  const fa::Shape s{B, H, N, d};
+  int st = fa::validate_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, s, scale, causal);
+  if (st != fa::kOk) return st;
+  st = fa::check_device();
+  if (st != fa::kOk) return st;
+  return fa::launch_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, stream) == hipSuccess
              ? fa::kOk
              : fa::kErrHip;
 }

@@ -40,6 +40,8 @@
 #include "fa_common.h"
 #include "fa_validate.h"
 
+#include <mutex>
+
 namespace fa {
 
 // Byte offset, inside a row-major LDS tile (rows of lds_row_bytes<DD>()) swizzled by
@@ -1012,6 +1014,49 @@ hipError_t launch_bwd_blocksparse(const void* q, const void* k, const void* v, c
                                                     per_head, ws, st)
               : launch_bwd_blocksparse_e<__bf16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, bm,
                                                  per_head, ws, st);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the workspace (D and LSE*log2(e), fully written by
+// the pre-pass before any kernel reads it) lives in this file-scope device
+// array, one copy per GPU.  Host code never passes the array's name to a
+// kernel (on the host it only stands for the symbol): the first call on each
+// device, with that device current, looks its device address up once and
+// keeps it.
+// ---------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                              int causal, hipStream_t st) {
+  if (bwd_workspace_bytes(Shape{B, H, N, d}) > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = scratch_ptr(&ws);
+  if (e != hipSuccess) return e;
+  return launch_bwd_e<__bf16>(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, ws, st);
 }
 
 hipError_t launch_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -14,7 +14,8 @@ namespace fa {
 // Status values mirror fa_status in include/fa.h.
 enum : int {
   kOk = 0, kErrNull = -1, kErrShape = -2, kErrHeadDim = -3, kErrScale = -4,
-  kErrAlign = -5, kErrWorkspace = -6, kErrDevice = -7, kErrHip = -8, kErrArg = -9
+  kErrAlign = -5, kErrWorkspace = -6, kErrDevice = -7, kErrHip = -8, kErrArg = -9,
+  kErrScratch = -10
 };
 
 struct Shape {
@@ -276,6 +277,37 @@ inline int validate_bwd_blocksparse(const void* q, const void* k, const void* v,
   return kOk;
 }
 
+// Scratch that the allocation-free backward (fa_bwd_noalloc) keeps in a
+// file-scope device array, one per GPU: the backward workspace of every call
+// must fit in it.  32 MiB holds the row terms of B*H*N up to about 4.19 M rows.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+
+// fa_bwd_noalloc: fa_bwd's checks without a caller workspace, plus the
+// scratch limit.
+inline int validate_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                                const void* dO, const void* dq, const void* dk, const void* dv,
+                                const Shape& s, float scale, int causal) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return kErrNull;
+  int st = check_common(s, scale, causal);
+  if (st != kOk) return st;
+  const void* all[9] = {q, k, v, o, lse, dO, dq, dk, dv};
+  for (const void* p : all)
+    if (!aligned16(p)) return kErrAlign;
+  if (bwd_workspace_bytes(s) > kNoAllocScratchBytes) return kErrScratch;
+  const size_t tb = size_t(tensor_elems(s)) * 2;
+  const size_t lb = size_t(s.B) * s.H * s.N * sizeof(float);
+  const void* ins[6] = {q, k, v, o, lse, dO};
+  const size_t insz[6] = {tb, tb, tb, tb, lb, tb};
+  const void* outs[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], tb, ins[j], insz[j])) return kErrArg;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], tb, outs[j], tb)) return kErrArg;
+  }
+  return kOk;
+}
+
 inline int check_dropout_p(float p) { return (std::isfinite(p) && p >= 0.0f && p < 1.0f) ? kOk : kErrArg; }
 
 inline const char* status_string(int st) {
@@ -290,6 +322,7 @@ inline const char* status_string(int st) {
     case kErrDevice: return "FA_ERR_DEVICE: the current device is not a gfx950 GPU";
     case kErrHip: return "FA_ERR_HIP: a HIP launch or runtime call failed";
     case kErrArg: return "FA_ERR_ARG: causal must be 0 or 1, counts and probabilities in range, and outputs must not alias inputs";
+    case kErrScratch: return "FA_ERR_SCRATCH: fa_bwd_noalloc needs fa_bwd_workspace_bytes() <= 32 MiB (B*H*N up to about 4.19 M rows)";
     default: return "unknown fa_status";
   }
 }

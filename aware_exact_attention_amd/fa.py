@@ -30,6 +30,8 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "fa_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
                         _c_int, _vp, _c_size_t, _vp]),
+    "fa_bwd_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                _c_int, _vp]),
     "fa_probe_mfma_bf16": (_c_int, [_c_int, _c_int, _vp, _vp]),
     "fa_fwd_splitkv_parts": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "fa_fwd_splitkv_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int, _c_int]),
@@ -176,6 +178,29 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, w
                             workspace.data_ptr(), workspace.numel(), _stream())
     if st != 0:
         raise FAError(st, name)
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, do, out, causal: bool = False, scale: float | None = None):
+    """bf16 backward through ``fa_bwd_noalloc``: the library's own per-GPU
+    scratch replaces the workspace, and ``out = (dq, dk, dv)`` must be
+    preallocated, so the call allocates nothing.  Calls that overlap on one
+    GPU share that scratch and must be ordered by the caller."""
+    lib = load()
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    _check(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = out
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    st = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale),
+                            int(bool(causal)), _stream())
+    if st != 0:
+        raise FAError(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

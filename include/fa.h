@@ -59,7 +59,8 @@ typedef enum {
   FA_ERR_WORKSPACE = -6, /* workspace missing or smaller than the matching *_workspace_bytes() */
   FA_ERR_DEVICE = -7,    /* current device is not gfx950, or its properties cannot be read */
   FA_ERR_HIP = -8,       /* a HIP launch or runtime call failed */
-  FA_ERR_ARG = -9        /* causal not 0/1, a part count out of range, or outputs alias inputs */
+  FA_ERR_ARG = -9,       /* causal not 0/1, a part count out of range, or outputs alias inputs */
+  FA_ERR_SCRATCH = -10   /* fa_bwd_noalloc: the problem needs more than its 32 MiB of scratch */
 } fa_status;
 
 /*
@@ -112,6 +113,27 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const void* dO, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_bwd_noalloc - fa_bwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same parameters, layout, results
+ * and kernels as fa_bwd, minus workspace and workspace_bytes; the caller still
+ * passes every input and output.  The workspace lives in a file-scope device
+ * array of 32 MiB inside libfa.so: each GPU the library runs on holds its own
+ * copy from the library's first use on that device until the process ends.
+ * The call allocates and frees nothing.  Limit: fa_bwd_workspace_bytes(B, H,
+ * N, d) <= 32 MiB (B*H*N up to about 4.19 M rows), else FA_ERR_SCRATCH before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array (the
+ * kernels overwrite it completely before reading it, so nothing needs
+ * clearing): calls that overlap in time on one GPU, on different streams or
+ * from different threads, race on it and must be ordered by the caller.
+ * The first call on a device looks the array's device address up
+ * (hipGetSymbolAddress) and keeps it for that device.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
  * fa_fwd_fp16, fa_bwd_fp16 - fp16 (IEEE binary16) versions of fa_fwd and

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 LIB = os.path.join(ROOT, "aware_exact_attention_amd", "libfa.so")
 
 ST = {"OK": 0, "NULL": -1, "SHAPE": -2, "HEAD_DIM": -3, "SCALE": -4, "ALIGN": -5, "WORKSPACE": -6,
-      "DEVICE": -7, "HIP": -8, "ARG": -9}
+      "DEVICE": -7, "HIP": -8, "ARG": -9, "SCRATCH": -10}
 
 
 def declared_functions():
@@ -37,7 +37,7 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_bytes", "fa_bwd", "fa_probe_mfma_bf16",
+    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_noalloc", "fa_probe_mfma_bf16",
                                            "fa_fwd_fp16", "fa_bwd_fp16", "fa_fwd_dropout", "fa_bwd_dropout",
                                            "fa_fwd_splitkv_parts", "fa_fwd_splitkv_workspace_bytes",
                                            "fa_fwd_splitkv", "fa_lse_merge", "fa_fwd_window",
@@ -144,6 +144,27 @@ def test_bwd_validation(lib, fn):
     assert call(dk=dq) == ST["ARG"]          # two outputs alias
     assert call(dv=v) == ST["ARG"]           # output aliases an input
     assert call(ws=dq) == ST["ARG"]          # workspace aliases an output
+
+
+def test_bwd_noalloc_validation(lib):
+    """fa_bwd_noalloc takes fa_bwd's arguments minus the workspace; a problem
+    whose workspace exceeds the library's 32 MiB scratch is refused before
+    anything is enqueued (4194304 rows fit, one more does not)."""
+    B, H, N, d = 1, 2, 16, 64
+    bufs = [_Buf(B * H * N * d * 2) for _ in range(9)]
+    q, k, v, o, lse, do, dq, dk, dv = [b.ptr for b in bufs]
+    f = lib.fa_bwd_noalloc
+    assert f(q, k, v, o, lse, None, dq, dk, dv, B, H, N, d, 0.125, 1, None) == ST["NULL"]
+    assert f(q, k, v, o, lse, do, dq, dk, dv, B, H, 0, d, 0.125, 1, None) == ST["SHAPE"]
+    assert f(q, k, v, o, lse, do, dq, dk, dv, B, H, N, 80, 0.125, 1, None) == ST["HEAD_DIM"]
+    assert f(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, -1.0, 1, None) == ST["SCALE"]
+    assert f(q, k, v, o, lse, do, dq + 4, dk, dv, B, H, N, d, 0.125, 1, None) == ST["ALIGN"]
+    assert f(q, k, v, o, lse, do, dq, dq, dv, B, H, N, d, 0.125, 1, None) == ST["ARG"]
+    assert f(q, k, v, o, lse, do, dq, dk, k, B, H, N, d, 0.125, 1, None) == ST["ARG"]
+    assert f(q, k, v, o, lse, do, dq, dk, dv, 1, 64, 65537, 64, 0.125, 0, None) == ST["SCRATCH"]
+    assert f(q, k, v, o, lse, do, dq, dk, dv, 1, 1, (1 << 22) + 1, 64, 0.125, 0, None) == ST["SCRATCH"]
+    assert lib.fa_bwd_workspace_bytes(1, 64, 65536, 64) == 32 << 20
+    assert lib.fa_bwd_workspace_bytes(1, 64, 65537, 64) > 32 << 20
 
 
 def test_probe_validation(lib):
@@ -349,6 +370,14 @@ int main() {
   EXPECT(bwd_workspace_bytes(Shape{1, 1, 8, 512}) == 0);
   EXPECT(split_count(Shape{1, 1, 256, 256}, 2) == 2);
   EXPECT(validate_lse_merge(mem[0], mem[1], 2, mem[2], mem[3], Shape{1, 1, 8, 256}) == kOk);
+  EXPECT(validate_bwd_noalloc(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8], s, 0.125f,
+                              1) == kOk);
+  EXPECT(validate_bwd_noalloc(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[6], mem[8], s, 0.125f,
+                              1) == kErrArg);
+  EXPECT(validate_bwd_noalloc(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8],
+                              Shape{1, 64, 65536, 64}, 0.125f, 1) != kErrScratch);
+  EXPECT(validate_bwd_noalloc(mem[0], mem[1], mem[2], mem[3], mem[4], mem[5], mem[6], mem[7], mem[8],
+                              Shape{1, 64, 65537, 64}, 0.125f, 1) == kErrScratch);
   EXPECT(check_dropout_p(0.0f) == kOk && check_dropout_p(0.999f) == kOk);
   EXPECT(check_dropout_p(1.0f) == kErrArg && check_dropout_p(-1e-9f) == kErrArg && check_dropout_p(NAN) == kErrArg);
   return fails ? 1 : 0;
