@@ -348,14 +348,23 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     auto p_pair = [&](auto qc, auto jc) {
       constexpr int qb = decltype(qc)::value, j = decltype(jc)::value;
       constexpr int g = j / 4, cg = qb * 4 + g;
-      const int qr = qb * 32 + 8 * g + 4 * half;
-      if constexpr (DROP && j % 4 == 0) keepg[cg] = keep_col4(dp, unsigned(qs + qr) >> 2, unsigned(key), unsigned(bh));
+      // dropout: the four lanes of a quad hold keys 4p .. 4p+3 and need the
+      // same call for each of the block's four 4-query groups; lane t draws
+      // group t (of this 32-query block) and the quad shares the results
+      if constexpr (DROP && j == 0) {
+        const unsigned t = lane & 3;
+        const unsigned mine =
+            keep_block_cols(dp, unsigned(qs + qb * 32 + 8 * t + 4 * half) >> 2, unsigned(key) >> 2, unsigned(bh));
+        const unsigned nib = quad_share_nibbles(mine, t);
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) keepg[qb * 4 + gg] = (nib >> (4 * gg)) & 0xFu;
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int e = j % 4 + t;
         const float p = exp2_fast(fmaf(s[qb][j + t], c, -l4[cg][e]));
         pk[qb][j + t] = p;
-        if constexpr (DROP) op[qb * 2 + (j >> 3)][(j + t) & 7] = (E)(((keepg[cg] >> e) & 1u) ? p : 0.f);
+        if constexpr (DROP) op[qb * 2 + (j >> 3)][(j + t) & 7] = (E)keep_or_zero(p, keepg[cg], e);
         else op[qb * 2 + (j >> 3)][(j + t) & 7] = (E)p;
       }
     };
@@ -367,7 +376,7 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
       for (int t = 0; t < 2; ++t) {
         const int e = j % 4 + t;
         float dpv = pd[qb][j + t];
-        if constexpr (DROP) dpv = ((keepg[cg] >> e) & 1u) ? dpv * dp.keep_scale : 0.f;
+        if constexpr (DROP) dpv = keep_or_zero(dpv * dp.keep_scale, keepg[cg], e);
         os[qb * 2 + (j >> 3)][(j + t) & 7] = (E)(pk[qb][j + t] * (dpv - d4[cg][e]));
       }
     };
@@ -688,14 +697,16 @@ dq_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__
     v8 db[T::PS];
     // dropout: registers 4m .. 4m+3 of a key block hold 4 consecutive keys of
     // this lane's query, one Philox block row; dP = Z * (dO V^T)
+    // as in the forward: lane t of a quad draws key group t, the quad shares
     unsigned keep = 0;
     if constexpr (DROP) {
+      const unsigned t = lane & 3;
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          keep |= keep_row4(dp, unsigned(qrow), unsigned(key0 + kb * 32 + acc_row(4 * m, lane)) >> 2, unsigned(bh))
-                  << (kb * 16 + 4 * m);
+      for (int kb = 0; kb < T::KB; ++kb) {
+        const unsigned key = unsigned(key0 + kb * 32 + 8 * t + 4 * half);
+        const unsigned mine = keep_block_rows(dp, unsigned(qrow) >> 2, key >> 2, unsigned(bh));
+        keep |= quad_share_nibbles(mine, t) << (kb * 16);
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
@@ -703,7 +714,7 @@ dq_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__
       for (int r = 0; r < 16; ++r) {
         const float pr = exp2_fast(fmaf(s[kb][r], c, -lq));
         float dpv = p[kb][r];
-        if constexpr (DROP) dpv = ((keep >> (kb * 16 + r)) & 1u) ? dpv * dp.keep_scale : 0.f;
+        if constexpr (DROP) dpv = keep_or_zero(dpv * dp.keep_scale, keep, kb * 16 + r);
         db[kb * 2 + (r >> 3)][r & 7] = (E)(pr * (dpv - dd));
       }
     // ---- dQ^T += K_j^T dS^T (k = key, in the accumulator's order)

@@ -233,6 +233,54 @@ __device__ __forceinline__ unsigned keep_col4(const DropArgs& dp, unsigned i4, u
   return bits;
 }
 
+// Keep bits of a whole 4 x 4 block, from one call: bit 4*e + b says whether
+// element (row 4*i4 + e, column 4*j4 + b) survives (word e, byte b).
+__device__ __forceinline__ unsigned keep_block_rows(const DropArgs& dp, unsigned i4, unsigned j4, unsigned bh) {
+  const u32x4 w = philox4x32_10(i4, j4, bh, 0u, dp.k0, dp.k1);
+  unsigned bits = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bits |= unsigned(((w[e] >> (8 * b)) & 0xFFu) >= dp.t) << (4 * e + b);
+  return bits;
+}
+
+// The same block with the bits transposed: bit 4*b + e.
+__device__ __forceinline__ unsigned keep_block_cols(const DropArgs& dp, unsigned i4, unsigned j4, unsigned bh) {
+  const u32x4 w = philox4x32_10(i4, j4, bh, 0u, dp.k0, dp.k1);
+  unsigned bits = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bits |= unsigned(((w[e] >> (8 * b)) & 0xFFu) >= dp.t) << (4 * b + e);
+  return bits;
+}
+
+// x if bit `bit` of `bits` is set, else +0: the bit is sign-extended into an
+// all-ones or all-zeros mask (one bit-field extract, no compare or select).
+__device__ __forceinline__ float keep_or_zero(float x, unsigned bits, int bit) {
+  const unsigned m = unsigned(int(bits << (31 - bit)) >> 31);
+  return __builtin_bit_cast(float, __builtin_bit_cast(unsigned, x) & m);
+}
+
+// x as held by lane M of this lane's quad (lanes 4q .. 4q+3): a DPP
+// quad_perm broadcast, VALU only.  Every lane of the quad must be active.
+template <int M>
+__device__ __forceinline__ unsigned quad_bcast(unsigned x) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)x, M * 0x55, 0xF, 0xF, false);
+}
+
+// The four lanes of a quad that need the same four Philox calls make one
+// each and share the results: lane t of the quad draws block `blk(t)` (16
+// keep bits, laid out so that the 4 bits lane t' needs are bits
+// 4*t' .. 4*t'+3) and every lane takes its nibble of each lane's block.
+// Returns nibble m (for the block drawn by lane m) at bits 4*m .. 4*m+3.
+__device__ __forceinline__ unsigned quad_share_nibbles(unsigned mine, unsigned t) {
+  const unsigned sh = 4 * t;
+  return ((quad_bcast<0>(mine) >> sh) & 0xFu) | (((quad_bcast<1>(mine) >> sh) & 0xFu) << 4) |
+         (((quad_bcast<2>(mine) >> sh) & 0xFu) << 8) | (((quad_bcast<3>(mine) >> sh) & 0xFu) << 12);
+}
+
 // Tile-skipping masks (beyond causal), shared by the forward and backward.
 // kMaskWindow: key j is visible to query i iff i - left <= j <= i + right (a
 // negative bound: no limit on that side).  kMaskBlocks: bm[h][i / 64][j / 64] != 0 keeps the 64 x 64 block,

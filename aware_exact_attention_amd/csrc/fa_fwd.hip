@@ -288,15 +288,18 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     // With dropout, bit kb*16 + r of `keep` says whether element (kb, r)
     // survives: registers 4m .. 4m+3 of a key block hold 4 consecutive keys of
     // this row, one Philox block row.
+    // The four lanes of a quad hold rows 4q .. 4q+3 (one Philox block row
+    // each) and the same keys, so they need the same four calls per key
+    // block: lane t makes the call of key group t and the quad shares it.
     unsigned keep = 0;
     if constexpr (DROP) {
+      const unsigned t = lane & 3;
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const unsigned key = unsigned(j * T::BC + kb * 32 + acc_row(4 * m, lane));
-          keep |= keep_row4(dp, unsigned(qrow), key >> 2, unsigned(bh)) << (kb * 16 + 4 * m);
-        }
+      for (int kb = 0; kb < T::KB; ++kb) {
+        const unsigned key = unsigned(j * T::BC + kb * 32 + 8 * t + 4 * half);
+        const unsigned mine = keep_block_rows(dp, unsigned(qrow) >> 2, key >> 2, unsigned(bh));
+        keep |= quad_share_nibbles(mine, t) << (kb * 16);
+      }
     }
     v8 pb[T::PS];
     float rs;
@@ -309,7 +312,7 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
           const float p = exp2_fast(fmaf(s[kb][r], c, -mu));
           rs += p;
           float pd = p;  // dropout: the kept P; the 1/(1-p) scale is applied to O at the end
-          if constexpr (DROP) pd = ((keep >> (kb * 16 + r)) & 1u) ? p : 0.f;
+          if constexpr (DROP) pd = keep_or_zero(p, keep, kb * 16 + r);
           pb[kb * 2 + (r >> 3)][r & 7] = (E)pd;
         }
     };
