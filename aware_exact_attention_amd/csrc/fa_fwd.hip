@@ -37,9 +37,10 @@ namespace fa {
 constexpr float kLazyRescale = 8.f;
 // The reference moves only on a tile where a lane's sum of P over its 32
 // elements reaches kSumBound (so some P >= 2^35), or while the row has none.
-// Until then every P < 2^40: with at most 2^22 keys and |V| < 2^8, O and l
-// stay below 2^70, far from fp32 overflow, and no precision is lost (a
-// floating-point P keeps its relative precision at any scale).  Rows whose
+// Until then every P < 2^40: with at most 2^22 keys, l stays below 2^62 and
+// O below 2^62 * max|V|, finite for |V| <= 2^64 (the documented input limit),
+// and no precision is lost (a floating-point P keeps its relative precision
+// at any scale).  Rows whose
 // scores keep climbing (large-spread scores) therefore rarely take the
 // rescale path, which every row of the wave then pays for.
 constexpr float kSumBound = 1099511627776.f;  // 2^40

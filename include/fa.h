@@ -28,6 +28,11 @@
  *   scale finite and > 0; B*H*N*d < 2^31 elements per tensor and
  *   (N + 256)*d*4 < 2^31 (one head's fp32 slab is addressed with 32-bit
  *   byte offsets).
+ * Magnitude limit (not checked): every |v| <= 2^64.  The forward accumulates
+ *   P V in fp32 with each P up to 2^40 times the row's current reference
+ *   before it renormalises, over up to 2^22 keys, so the accumulators stay
+ *   below 2^126 within that limit; larger values can overflow them to
+ *   inf/NaN where the exact result is finite.
  * Causal mask: key j is visible to query i iff j <= i (queries and keys have
  *   the same length N).
  * Log-sum-exp: lse[b][h][i] = ln( sum over visible j of exp(scale * q_i . k_j) ),

@@ -246,6 +246,29 @@ def test_climbing_scores(gpu_lib, slope, causal):
     check_grad_bound(tag, "dK", _np(dk), rk, bk)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_values_with_lagging_reference(gpu_lib, causal):
+    """V at the documented magnitude limit's scale (|V| up to about 2^62) with
+    scores climbing at 0.3 per key, so the row's reference lags and P reaches
+    nearly 2^40 before it moves: the fp32 accumulators must stay finite and O
+    must be V's scale times the oracle's O of the unscaled values (2^60 is a
+    power of two, so the scaled bf16 inputs are exact)."""
+    N, d = 1000, 64
+    q, k, v = make_inputs(1, 2, N, d, "bf16", seed=330)
+    q = q * 0.05
+    q[..., 0] = 1.0
+    k = k * 0.05
+    k[..., 0] = (torch.arange(N, dtype=torch.float32) * 0.3).to(torch.bfloat16)
+    big = 2.0 ** 60
+    vb = (v.float() * big).to(torch.bfloat16)
+    assert torch.equal(vb.float() / big, v.float())
+    o, lse = _fwd(gpu_lib, q, k, vb, causal, 1.0)
+    ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), 1.0, causal)
+    tag = f"large_values causal={causal}"
+    check_o(tag, _np(o) / big, ro)
+    check_lse(tag, _np(lse), rl)
+
+
 @pytest.mark.parametrize("name", ["gpt2", "gpt2_causal"])
 def test_gpt2_shape(gpu_lib, name):
     w = WORKLOADS[name]
