@@ -327,7 +327,9 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
       const float mxr = halves_max(mx) * c;
       const float m_new = (mxr > m + kLazyRescale) ? mxr : m;
       const float mu_new = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet in this row
-      const float alpha = exp2_fast(mu - mu_new);  // O and l are still 0 while m is -inf
+      // O and l are still 0 while m is -inf: no factor then (exp2(0 - mu_new)
+      // overflows when every score of the first visible tile is below -128)
+      const float alpha = m == -INFINITY ? 0.f : exp2_fast(mu - mu_new);
       m = m_new;
       mu = mu_new;
       l *= alpha;

@@ -246,6 +246,27 @@ def test_climbing_scores(gpu_lib, slope, causal):
     check_grad_bound(tag, "dK", _np(dk), rk, bk)
 
 
+@pytest.mark.parametrize("H,N,d", [(2, 300, 64), (2, 300, 128), (128, 200, 128), (128, 200, 64),
+                                   (128, 600, 128), (2, 300, 256)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_scores_far_below_zero(gpu_lib, H, N, d, causal):
+    """Every score near -150 (scale 1): about -216 in log2 units, so the first
+    reference of each row lies far below 0, where exp2 of its negative
+    overflows.  Softmax does not change under a shift of the scores, so O is
+    an ordinary weighted mean of V and the LSE is near -150.  The shapes take
+    each workgroup size of the forward at d = 64, 128 and 256."""
+    q, k, v = make_inputs(1, H, N, d, "bf16", seed=330 + H + N + d)
+    q = q * 0.05
+    q[..., 0] = 1.0
+    k = k * 0.05
+    k[..., 0] = -150.0
+    o, lse = _fwd(gpu_lib, q, k, v, causal, 1.0)
+    ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), 1.0, causal)
+    name = f"scores far below zero H={H} N={N} d={d} causal={causal}"
+    check_o(name, _np(o), ro)
+    check_lse(name, _np(lse), rl)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_values_with_lagging_reference(gpu_lib, causal):
     """V at the documented magnitude limit's scale (|V| up to about 2^62) with
