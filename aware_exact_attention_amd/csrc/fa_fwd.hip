@@ -10,10 +10,12 @@
 // Software 2026(1) p.218 survey.  The per-row statistic written for the
 // backward pass is LSE = m + ln(l).
 //
-// gfx950 mapping of the bf16 kernel (one workgroup = 2, 4 or 8 waves = 64,
-// 128 or 256 query rows of one head):
+// gfx950 mapping of the bf16 kernel (one workgroup = 4 or 8 waves = 128 or
+// 256 query rows of one head; on grids too small to give every SIMD two
+// waves, 8 waves = 128 or 64 rows whose keys are split over 2 or 4 waves):
 //  * each wave owns 32 whole query rows, so the row statistics m and l never
-//    leave the wave (no inter-wave exchange);
+//    leave the wave until the key parts of a row are merged (Eq. (2)) at the
+//    end;
 //  * the wave computes S^T = K_j Q_i^T with v_mfma_f32_32x32x16_bf16: the
 //    accumulator puts one query per lane (lane % 32) and that query's keys in
 //    the lane's registers, so the row max and row sum are mostly in-lane
@@ -46,12 +48,14 @@ constexpr float kLazyRescale = 8.f;
 constexpr float kSumBound = 1099511627776.f;  // 2^40
 
 
-template <int D, int NW_>
+template <int D, int NW_, int KQ_ = 1>
 struct FwdTile {
-  static constexpr int NW = NW_;                  // waves per workgroup (2, 4 or 8)
+  static constexpr int NW = NW_;                  // waves per workgroup (4 or 8)
+  static constexpr int KQ = KQ_;                  // key parts per workgroup (1, 2 or 4)
+  static constexpr int RG = NW / KQ;              // 32-row groups per workgroup
   static constexpr int NT = 64 * NW;              // threads per workgroup
-  static constexpr int BR = 32 * NW;              // query rows per workgroup
-  static constexpr int BC = 64;                   // keys per KV tile
+  static constexpr int BR = 32 * RG;              // query rows per workgroup
+  static constexpr int BC = KQ == 4 ? 32 : 64;    // keys per KV tile
   static constexpr int KS = D / 16;               // 16-wide k steps of Q K^T
   static constexpr int DB = D / 32;               // 32-column blocks of O
   static constexpr int KB = BC / 32;              // 32-key blocks of S
@@ -60,8 +64,9 @@ struct FwdTile {
   static constexpr int GRS = D * 2;               // bytes per row in HBM
   static constexpr int TILE = BC * RS;            // bytes of one K or V tile
   static constexpr int STAGE = 2 * TILE;          // K tile then V tile
-  static constexpr int LPW = TILE / 1024 / NW;    // 1 KiB direct-to-LDS loads per wave per tile
-  static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads over the waves");
+  static constexpr int LPW = TILE / 1024 / RG;    // 1 KiB direct-to-LDS loads per wave per tile
+  static_assert(TILE % (1024 * RG) == 0, "tile must split into 1 KiB loads over the waves of a key part");
+  static_assert(NW % KQ == 0, "every key part has the same row groups");
 };
 
 // Key-split mode: the keys of every row are cut into ranges of TPS whole
@@ -77,24 +82,35 @@ struct SplitArgs {
 };
 
 
-template <typename E, int D, bool CAUSAL, int NW, bool SPLIT, int MODE, bool DROP>
+template <typename E, int D, bool CAUSAL, int NW, bool SPLIT, int MODE, bool DROP, int KQ = 1>
 __global__ void __launch_bounds__(64 * NW, D == 256 ? 1 : 8 / NW)
 fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V, E* __restrict__ O,
            float* __restrict__ LSE, int N, int Tr, float c, SplitArgs sp, MaskArgs mk, DropArgs dp) {
-  using T = FwdTile<D, NW>;
+  using T = FwdTile<D, NW, KQ>;
   using v8 = typename Vec<E>::v8;
   using v4 = typename Vec<E>::v4;
   constexpr bool WINDOW = MODE == kMaskWindow, BLOCKS = MODE == kMaskBlocks;
+  static_assert(KQ == 1 || (NW == 8 && D <= 128 && !SPLIT && MODE == kMaskDense && !DROP),
+                "key parts only in the eight-wave dense or causal forward");
   static_assert(!(SPLIT && MODE != kMaskDense), "key split only with the dense or causal mask");
   static_assert(!DROP || (!SPLIT && MODE == kMaskDense), "dropout only on the plain forward");
   static_assert(!BLOCKS || (T::BC == kMaskBlock && T::BR == 2 * kMaskBlock), "mask blocks are key tiles and half a row block");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * T::STAGE];
+  // The two stages are separate arrays: with one array the compiler cannot
+  // tell the direct loads of the next tile from the reads of this one and
+  // waits for those loads before the transposing V reads.
+  // Stage s of key part p: (s ? smem1 : smem0) + p * STAGE.
+  __shared__ __attribute__((aligned(1024))) char smem0[KQ * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[KQ * T::STAGE];
   __shared__ unsigned short tlist[BLOCKS ? kMaxMaskTiles : 1];
   __shared__ int tcount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses for the direct loads
+  // With KQ key parts, wave w takes the rows of row group w % RG and the keys
+  // of part w / RG: the parts of a row run side by side on different SIMDs.
+  const int rg = KQ == 1 ? wave : wave % T::RG;
+  const int kp = KQ == 1 ? 0 : wave / T::RG;
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int per_head = SPLIT ? Tr * sp.S : Tr;  // the parts of a query block are adjacent
@@ -119,7 +135,7 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
 
   // Q fragment (B operand of S^T = K Q^T): row qrow, columns 16*s + 8*half .. +7.
   // Rows past N read as zero (buffer bounds).
-  const int wq0 = q0 + wave * 32;
+  const int wq0 = q0 + rg * 32;
   const int qrow = wq0 + l32;
   v8 qf[T::KS];
   {
@@ -175,25 +191,34 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     }
     __syncthreads();
   }
-  const int cnt = BLOCKS ? tcount : nt - j0;
-  auto tile_at = [&](int idx) { return BLOCKS ? int(tlist[idx]) : j0 + idx; };
+  // Key part kp takes tiles [pj0, pj1) of the workgroup's [j0, nt), tpk
+  // steps for every part, so that all waves meet the same barriers.
+  int tpk = nt - j0, pj0 = j0, pj1 = nt;
+  if (KQ > 1) {
+    tpk = (nt - j0 + KQ - 1) / KQ;
+    pj0 = j0 + kp * tpk;
+    pj1 = min(nt, pj0 + tpk);
+  }
+  const int cnt = BLOCKS ? tcount : tpk;                  // steps of the workgroup
+  const int cnt_w = BLOCKS ? cnt : max(0, pj1 - pj0);     // steps with a tile of this wave's part
+  auto tile_at = [&](int idx) { return BLOCKS ? int(tlist[idx]) : pj0 + idx; };
   auto wave_needs = [&](int j) {
     if (!wave_active || j >= nt_w || j < w0) return false;
     return !BLOCKS || bm_row[j] != 0;
   };
 
   // Direct-to-LDS tile loads: load i of this wave fills LDS bytes
-  // [(wave*LPW + i) KiB, +1 KiB) of the tile; lane l brings the 16 bytes that
+  // [(rg*LPW + i) KiB, +1 KiB) of its part's tile; lane l brings the 16 bytes that
   // belong at byte 16*l of that range under the swizzle.
   int goff[T::LPW];
 #pragma unroll
-  for (int i = 0; i < T::LPW; ++i) goff[i] = swz_src<D>((wave * T::LPW + i) * 1024 + 16 * lane);
+  for (int i = 0; i < T::LPW; ++i) goff[i] = swz_src<D>((rg * T::LPW + i) * 1024 + 16 * lane);
   auto issue_loads = [&](int j, int stage) {
     const int key0 = j * T::BC;
     const int bytes = (N - key0) * T::GRS;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + size_t(key0) * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + size_t(key0) * D, bytes);
-    char* kdst = smem + stage * T::STAGE + wave * T::LPW * 1024;
+    char* kdst = (stage ? smem1 : smem0) + kp * T::STAGE + rg * T::LPW * 1024;
 #pragma unroll
     for (int i = 0; i < T::LPW; ++i)
       load_lds16(rk, kdst + i * 1024, goff[i]);
@@ -230,33 +255,33 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   float l = 0.f;        // running sum over this lane's half of the keys
 
   auto compute = [&](int j, const char* base) {
-    // ---- S^T = K_j Q^T: two independent 32-key chains; K operands are read
+    // ---- S^T = K_j Q^T: one independent chain per 32-key block; K operands are read
     // KPF k steps ahead, an order pinned by scheduling barriers (left alone,
     // the scheduler pulls each read next to its MFMA and the LDS latency shows)
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    f32x16 s[T::KB];
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) s[kb] = f32x16{};
     constexpr int KPF = 2;
-    v8 kr[KPF][2];
+    v8 kr[KPF][T::KB];
 #pragma unroll
-    for (int st = 0; st < KPF; ++st) {
-      kr[st][0] = *reinterpret_cast<const v8*>(base + kof[st]);
-      kr[st][1] = *reinterpret_cast<const v8*>(base + kof[st] + 32 * T::RS);
-    }
+    for (int st = 0; st < KPF; ++st)
 #pragma unroll
-    for (int st = 0; st < T::KS; ++st) {
-      s0 = mfma32(kr[st % KPF][0], qf[st], s0);
-      s1 = mfma32(kr[st % KPF][1], qf[st], s1);
-      if (st + KPF < T::KS) {
-        kr[st % KPF][0] = *reinterpret_cast<const v8*>(base + kof[st + KPF]);
-        kr[st % KPF][1] = *reinterpret_cast<const v8*>(base + kof[st + KPF] + 32 * T::RS);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KPF, 0);
+      for (int kb = 0; kb < T::KB; ++kb) kr[st][kb] = *reinterpret_cast<const v8*>(base + kof[st] + kb * 32 * T::RS);
 #pragma unroll
     for (int st = 0; st < T::KS; ++st) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (st + KPF < T::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) s[kb] = mfma32(kr[st % KPF][kb], qf[st], s[kb]);
+      if (st + KPF < T::KS)
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb)
+          kr[st % KPF][kb] = *reinterpret_cast<const v8*>(base + kof[st + KPF] + kb * 32 * T::RS);
     }
-    f32x16 s[2] = {s0, s1};
+    __builtin_amdgcn_sched_group_barrier(0x100, T::KB * KPF, 0);
+#pragma unroll
+    for (int st = 0; st < T::KS; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, T::KB, 0);
+      if (st + KPF < T::KS) __builtin_amdgcn_sched_group_barrier(0x100, T::KB, 0);
+    }
     // ---- masks: keys past N and, if causal, keys after the query; for a
     // window, keys outside [qrow - left, qrow + right].  Only tiles that cross
     // one of these edges for some row of the wave pay for the element mask.
@@ -363,15 +388,17 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
 
   // step idx: tile tile_at(idx) from stage `stage`, loads of the next tile into the other
   auto step = [&](int idx, int stage) {
-    if (idx + 1 < cnt) issue_loads(tile_at(idx + 1), stage ^ 1);
-    const int j = tile_at(idx);
-    if (wave_needs(j)) compute(j, smem + stage * T::STAGE);
+    if (idx + 1 < cnt_w) issue_loads(tile_at(idx + 1), stage ^ 1);
+    if (idx < cnt_w) {
+      const int j = tile_at(idx);
+      if (wave_needs(j)) compute(j, (stage ? smem1 : smem0) + kp * T::STAGE);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the next tile have landed
     __syncthreads();
   };
 
   if (cnt > 0) {  // uniform over the workgroup; an empty key part or mask row skips the sweep
-    issue_loads(tile_at(0), 0);
+    if (cnt_w > 0) issue_loads(tile_at(0), 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     int idx = 0;
@@ -382,6 +409,44 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     if (idx < cnt) step(idx, 0);
   }
 
+  if constexpr (KQ > 1) {
+    // The key parts of each row meet in LDS, by the merge rule of Eq. (2) in
+    // halving rounds: parts [h, 2h) hand their (o, m, l) to parts [0, h).  A
+    // part that saw no key has m = -inf, l = 0, o = 0 and weight 0.  The
+    // stages are free (every wave has passed the sweep's last barrier).
+    static_assert((KQ / 2) * T::RG * T::DB * 16 * 64 * 4 <= KQ * T::STAGE, "merge buffer fits in the stages");
+    float* xo = reinterpret_cast<float*>(smem0);  // [h][RG][DB][16][64]
+    float* xs = reinterpret_cast<float*>(smem1);  // [h][RG][2][64]: m, l
+#pragma unroll
+    for (int h = KQ / 2; h >= 1; h /= 2) {
+      if (kp >= h && kp < 2 * h) {
+        const int slot = (kp - h) * T::RG + rg;
+#pragma unroll
+        for (int b = 0; b < T::DB; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) xo[((slot * T::DB + b) * 16 + e) * 64 + lane] = o[b][e];
+        xs[(slot * 2 + 0) * 64 + lane] = m;
+        xs[(slot * 2 + 1) * 64 + lane] = l;
+      }
+      __syncthreads();
+      if (kp < h) {
+        const int slot = kp * T::RG + rg;
+        const float m1 = xs[(slot * 2 + 0) * 64 + lane];
+        const float l1 = xs[(slot * 2 + 1) * 64 + lane];
+        const float mn = fmaxf(m, m1);
+        const float a0 = m == -INFINITY ? 0.f : exp2_fast(m - mn);
+        const float a1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - mn);
+        l = l * a0 + l1 * a1;
+#pragma unroll
+        for (int b = 0; b < T::DB; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[b][e] = o[b][e] * a0 + xo[((slot * T::DB + b) * 16 + e) * 64 + lane] * a1;
+        m = mn;
+      }
+      if (h > 1) __syncthreads();  // the next round's writers have read theirs
+    }
+    if (kp > 0) return;
+  }
   if (!wave_active) return;
   const float lt = halves_sum(l);
   if (SPLIT) {
@@ -530,25 +595,44 @@ static hipError_t launch_fwd_nw(const void* q, const void* k, const void* v, voi
   return hipGetLastError();
 }
 
+// Eight waves with KQ key parts: 32*8/KQ rows per workgroup, each row's keys
+// split over KQ waves on different SIMDs and merged in LDS at the end.
+template <typename E, int D, bool CAUSAL, int KQ>
+static hipError_t launch_fwd_kq(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                int N, float scale, hipStream_t st) {
+  using T = FwdTile<D, 8, KQ>;
+  const int Tr = (N + T::BR - 1) / T::BR;
+  const long long G = (long long)B * H * Tr;
+  if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, 8, false, kMaskDense, false, KQ>), dim3((unsigned)G), dim3(T::NT), 0,
+                     st, (const E*)q, (const E*)k, (const E*)v, (E*)o, lse, N, Tr, scale * kLog2e,
+                     SplitArgs{1, 0, nullptr, nullptr, 0, 0}, MaskArgs{}, DropArgs{});
+  return hipGetLastError();
+}
+
 // Eight waves (256 rows, one workgroup per CU) stream each K/V tile once for
 // twice the rows of four waves (128 rows, two workgroups per CU), halving the
 // tile loads and LDS writes per row; used at d = 128 and 96 when that grid still
 // covers every CU, causal or not (causal grids dispatch their longest row
 // blocks first; measured 2 % faster than 128-row blocks at B2 H8 N16000 and
 // B1 H8 N16384, even at B4 H16 N4096).  d = 64 keeps four waves: its tiles
-// carry half the MFMA work per barrier (measured slower with 8 waves).  A grid
-// of 128-row blocks that leaves CUs idle (B*H*ceil(N/128) < 256) is cut into
-// 64-row blocks of two waves instead, which spreads the same waves over twice
-// as many CUs: 4-8 % faster at d = 128 for B1 H8 N1024-2048, neutral at d = 64.
+// carry half the MFMA work per barrier (measured slower with 8 waves).  Grids
+// with too few rows for two waves per SIMD split each row's keys instead:
+// 128-row workgroups with two key parts when 256-row blocks leave CUs idle
+// but 128-row blocks do not (d = 128, 96), 64-row workgroups with four key
+// parts when even 128-row blocks leave CUs idle (d <= 128): 1.1-1.7x faster
+// at B1 H8 N1024-4096 d128, B1 H4 N4096 causal and B1 H2 N8192 d64.
 template <typename E, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                int N, float scale, hipStream_t st) {
   const long long G8 = (long long)B * H * ((N + FwdTile<D, 8>::BR - 1) / FwdTile<D, 8>::BR);
   if constexpr (D == 128 || D == 96)
     if (G8 >= kNumCUs) return launch_fwd_nw<E, D, CAUSAL, 8>(q, k, v, o, lse, B, H, N, scale, st);
-  if constexpr (D == 128 || D == 96) {
+  if constexpr (D <= 128) {
     const long long G4 = (long long)B * H * ((N + FwdTile<D, 4>::BR - 1) / FwdTile<D, 4>::BR);
-    if (G4 < kNumCUs) return launch_fwd_nw<E, D, CAUSAL, 2>(q, k, v, o, lse, B, H, N, scale, st);
+    if (G4 < kNumCUs) return launch_fwd_kq<E, D, CAUSAL, 4>(q, k, v, o, lse, B, H, N, scale, st);
+    if constexpr (D != 64)
+      if (G8 < kNumCUs) return launch_fwd_kq<E, D, CAUSAL, 2>(q, k, v, o, lse, B, H, N, scale, st);
   }
   return launch_fwd_nw<E, D, CAUSAL, 4>(q, k, v, o, lse, B, H, N, scale, st);
 }

@@ -254,7 +254,9 @@ def test_all_scores_far_below_zero(gpu_lib, H, N, d, causal):
     reference of each row lies far below 0, where exp2 of its negative
     overflows.  Softmax does not change under a shift of the scores, so O is
     an ordinary weighted mean of V and the LSE is near -150.  The shapes take
-    each workgroup size of the forward at d = 64, 128 and 256."""
+    each launch shape of the forward: 64-row workgroups with four key parts,
+    128-row workgroups with two (d = 128) or four waves (d = 64), 256-row
+    workgroups, and d = 256."""
     q, k, v = make_inputs(1, H, N, d, "bf16", seed=330 + H + N + d)
     q = q * 0.05
     q[..., 0] = 1.0
@@ -315,14 +317,17 @@ def test_ragged_bf16_many_heads(gpu_lib, N, d, causal):
 
 
 @pytest.mark.parametrize("H,N", [(8, 300), (128, 200), (128, 600)])
-@pytest.mark.parametrize("d", [96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_each_workgroup_width(gpu_lib, H, N, d, causal):
-    """At d = 96 and 128 the forward picks its workgroup height from the grid
-    size: B1 H8 N300 leaves CUs idle with 128-row blocks (24 blocks) and runs
-    64-row blocks, B1 H128 N200 fills the 256 CUs with 128-row blocks but not
-    with 256-row ones, and B1 H128 N600 fills them with 256-row blocks.
-    Each width, with a ragged last block, is compared in full."""
+    """The forward picks its workgroup shape from the grid size.  B1 H8 N300
+    leaves CUs idle with 128-row blocks (24 blocks): 64-row workgroups of
+    eight waves, each row's keys split over four waves (32-key tiles) and
+    merged in LDS.  At d = 96 and 128, B1 H128 N200 fills the 256 CUs with
+    128-row blocks but not with 256-row ones: 128-row workgroups of eight
+    waves with two key parts; at d = 64 it runs four-wave 128-row blocks.
+    B1 H128 N600 fills them with 256-row blocks (d = 64: 128-row blocks).
+    Each shape, with a ragged last block, is compared in full."""
     q, k, v = make_inputs(1, H, N, d, "bf16", seed=800 + H + N + d)
     scale = d ** -0.5
     o, lse = _fwd(gpu_lib, q, k, v, causal, scale)
