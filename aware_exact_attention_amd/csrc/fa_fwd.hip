@@ -90,7 +90,7 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   using v8 = typename Vec<E>::v8;
   using v4 = typename Vec<E>::v4;
   constexpr bool WINDOW = MODE == kMaskWindow, BLOCKS = MODE == kMaskBlocks;
-  static_assert(KQ == 1 || (NW == 8 && D <= 128 && !SPLIT && MODE == kMaskDense && !DROP),
+  static_assert(KQ == 1 || (NW == 8 && D <= 128 && !SPLIT && MODE == kMaskDense),
                 "key parts only in the eight-wave dense or causal forward");
   static_assert(!(SPLIT && MODE != kMaskDense), "key split only with the dense or causal mask");
   static_assert(!DROP || (!SPLIT && MODE == kMaskDense), "dropout only on the plain forward");
@@ -597,16 +597,16 @@ static hipError_t launch_fwd_nw(const void* q, const void* k, const void* v, voi
 
 // Eight waves with KQ key parts: 32*8/KQ rows per workgroup, each row's keys
 // split over KQ waves on different SIMDs and merged in LDS at the end.
-template <typename E, int D, bool CAUSAL, int KQ>
+template <typename E, int D, bool CAUSAL, int KQ, bool DROP = false>
 static hipError_t launch_fwd_kq(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                                int N, float scale, hipStream_t st) {
+                                int N, float scale, hipStream_t st, DropArgs dp = DropArgs{}) {
   using T = FwdTile<D, 8, KQ>;
   const int Tr = (N + T::BR - 1) / T::BR;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, 8, false, kMaskDense, false, KQ>), dim3((unsigned)G), dim3(T::NT), 0,
+  hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, 8, false, kMaskDense, DROP, KQ>), dim3((unsigned)G), dim3(T::NT), 0,
                      st, (const E*)q, (const E*)k, (const E*)v, (E*)o, lse, N, Tr, scale * kLog2e,
-                     SplitArgs{1, 0, nullptr, nullptr, 0, 0}, MaskArgs{}, DropArgs{});
+                     SplitArgs{1, 0, nullptr, nullptr, 0, 0}, MaskArgs{}, dp);
   return hipGetLastError();
 }
 
@@ -662,13 +662,21 @@ hipError_t launch_fwd_fp16(const void* q, const void* k, const void* v, void* o,
 
 // Forward with dropout on P: the plain forward's tiles, with the keep bits of
 // each tile drawn in the kernel; eight-wave workgroups for non-causal d = 128
-// grids that cover every CU, four waves otherwise.
+// grids that cover every CU, key parts on the grids where the plain forward
+// uses them (a keep bit depends on the row and the key only), four waves
+// otherwise.
 template <typename E, int D, bool CAUSAL>
 static hipError_t launch_fwd_dropout_t(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                        int H, int N, float scale, const DropArgs& dp, hipStream_t st) {
   const long long G8 = (long long)B * H * ((N + FwdTile<D, 8>::BR - 1) / FwdTile<D, 8>::BR);
   if constexpr (D == 128)
     if (!CAUSAL && G8 >= kNumCUs) return launch_fwd_nw<E, D, CAUSAL, 8, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
+  if constexpr (D <= 128) {
+    const long long G4 = (long long)B * H * ((N + FwdTile<D, 4>::BR - 1) / FwdTile<D, 4>::BR);
+    if (G4 < kNumCUs) return launch_fwd_kq<E, D, CAUSAL, 4, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
+    if constexpr (D != 64)
+      if (G8 < kNumCUs) return launch_fwd_kq<E, D, CAUSAL, 2, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
+  }
   return launch_fwd_nw<E, D, CAUSAL, 4, true>(q, k, v, o, lse, B, H, N, scale, st, dp);
 }
 
