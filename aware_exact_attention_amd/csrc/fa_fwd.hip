@@ -55,7 +55,7 @@ struct FwdTile {
   static constexpr int RG = NW / KQ;              // 32-row groups per workgroup
   static constexpr int NT = 64 * NW;              // threads per workgroup
   static constexpr int BR = 32 * RG;              // query rows per workgroup
-  static constexpr int BC = KQ == 4 ? 32 : 64;    // keys per KV tile
+  static constexpr int BC = KQ == 4 && D > 64 ? 32 : 64;  // keys per KV tile (four parts' stages in 128 KiB)
   static constexpr int KS = D / 16;               // 16-wide k steps of Q K^T
   static constexpr int DB = D / 32;               // 32-column blocks of O
   static constexpr int KB = BC / 32;              // 32-key blocks of S
