@@ -485,98 +485,193 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: no bf16 rounding anywhere.  Four lanes share one query row (each
-// holds a quarter of the columns of q and of the output), a workgroup covers
-// 64 rows, and K/V tiles of 32 keys are staged in LDS and read by broadcast.
+// fp32 path: nothing is rounded below fp32.  Both products run on the fp32
+// matrix cores (v_mfma_f32_32x32x2_f32, same accumulator layout as the bf16
+// MFMA): four waves of 32 query rows per workgroup, one query per lane,
+// 32-key K/V tiles staged in LDS (fp32 rows padded by 16 bytes, so the
+// 128-bit K reads of 16 consecutive rows fall on distinct banks), double
+// buffered through registers.
+//  * S^T = K_j Q^T: k step st pairs dims st (lanes l < 32) and D/2 + st
+//    (lanes l >= 32), so a lane's Q fragment is one contiguous half row and
+//    its K operands come four k steps at a time from one 128-bit LDS read;
+//  * O^T += V_j^T P^T: k step r pairs the two keys that element r of the
+//    score accumulator holds in lanes l and l + 32, so P^T is the lane's own
+//    score register and V^T one float per lane of a V tile row.
+// The online softmax is the bf16 kernel's (lazy reference, exp2 with the
+// scale folded into one FMA).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256)
-fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-               float* __restrict__ O, float* __restrict__ LSE, int N, int Tr, float scale) {
-  constexpr int QL = 4, BR = 64, BC = 32, NCH = D / 4 / QL;  // float4 chunks per lane
-  __shared__ __attribute__((aligned(16))) float Ks[BC * D];
-  __shared__ __attribute__((aligned(16))) float Vs[BC * D];
-  const int tid = threadIdx.x;
-  const int sub = tid & (QL - 1);
-  const int tile = blockIdx.x;
-  const int bh = tile / Tr;
-  const int q0 = (tile - bh * Tr) * BR;
-  const int qrow = q0 + tid / QL;
-  const size_t head = size_t(bh) * N * D;
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
 
-  // lane holds columns 4*(i*QL + sub) .. +3 for i < NCH
-  f32x4 q[NCH], o[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    q[i] = qrow < N ? *reinterpret_cast<const f32x4*>(Q + head + size_t(qrow) * D + 4 * (i * QL + sub)) : f32x4{};
-    o[i] = f32x4{};
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, D == 256 ? 1 : 2)
+fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+               float* __restrict__ O, float* __restrict__ LSE, int N, int Tr, float c) {
+  constexpr int BR = 128, BC = 32, H2 = D / 2, DB = D / 32;
+  constexpr int RSF = D + 4;               // floats per LDS row
+  constexpr int TILEF = BC * RSF;          // floats of one K or V tile
+  constexpr int LDV = D / 4;               // float4 per row
+  constexpr int LPT = BC * LDV / 256;      // float4 of the K (and of the V) tile each thread moves
+  __shared__ __attribute__((aligned(16))) float sm[2][2 * TILEF];  // stage: K tile, then V tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  int bh, it;
+  if (CAUSAL) {
+    int r;
+    causal_order(blockIdx.x, gridDim.x / Tr, Tr, bh, r);
+    it = Tr - 1 - r;  // longest rows first
+  } else {
+    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    bh = t / Tr;
+    it = t - bh * Tr;
   }
-  float m = -INFINITY, l = 0.f;
+  const int q0 = it * BR;
+  const size_t head = size_t(bh) * N * D;
+  const int head_bytes = N * D * 4;
+  const int wq0 = q0 + wave * 32;
+  const int qrow = wq0 + l32;
+
+  // Q fragment: row qrow, dims half*D/2 .. +D/2-1 (rows past N read as zero)
+  float qf[H2];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head, head_bytes);
+#pragma unroll
+    for (int t = 0; t < H2 / 4; ++t) {
+      // (cast the whole vector: a bit cast of one vector element reads element 0)
+      const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (qrow * D + half * H2 + 4 * t) * 4, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * t + e] = w[e];
+    }
+  }
+
   const int Tc = (N + BC - 1) / BC;
-  const int nt = CAUSAL ? min(Tc, (min(q0 + BR, N) - 1) / BC + 1) : Tc;
-  for (int j = 0; j < nt; ++j) {
+  int nt = Tc;
+  if (CAUSAL) nt = min(Tc, (min(q0 + BR, N) - 1) / BC + 1);
+  const bool wave_active = wq0 < N;
+  int nt_w = nt;
+  if (CAUSAL && wave_active) nt_w = min(nt, (min(wq0 + 32, N) - 1) / BC + 1);
+
+  // Tile j through registers: thread tid moves float4 number tid + 256 i of
+  // the K tile and of the V tile; keys past N read as zero.
+  f32x4 kreg[LPT], vreg[LPT];
+  auto load_tile = [&](int j) {
     const int key0 = j * BC;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head + size_t(key0) * D, (N - key0) * D * 4);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head + size_t(key0) * D, (N - key0) * D * 4);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int idx = tid + 256 * i, row = idx / LDV, col = idx % LDV;
+      kreg[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (row * D + 4 * col) * 4, 0, 0));
+      vreg[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (row * D + 4 * col) * 4, 0, 0));
+    }
+  };
+  auto store_tile = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int idx = tid + 256 * i, row = idx / LDV, col = idx % LDV;
+      *reinterpret_cast<f32x4*>(&sm[stage][row * RSF + 4 * col]) = kreg[i];
+      *reinterpret_cast<f32x4*>(&sm[stage][TILEF + row * RSF + 4 * col]) = vreg[i];
+    }
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) o[b] = f32x16{};
+  float m = -INFINITY;  // reference of scale*log2(e)*score
+  float mu = 0.f;       // m, or 0 while m is -inf
+  float l = 0.f;        // running sum over this lane's half of the keys
+
+  auto compute = [&](int j, const float* ks, const float* vs) {
+    // ---- S^T = K_j Q^T, K operands read two 128-bit groups ahead
+    f32x16 s = f32x16{};
+    const float* kp = ks + l32 * RSF + half * H2;
+    f32x4 kq[2] = {*reinterpret_cast<const f32x4*>(kp), *reinterpret_cast<const f32x4*>(kp + 4)};
+#pragma unroll
+    for (int t = 0; t < H2 / 4; ++t) {
+      const f32x4 kv = kq[t & 1];
+      if (t + 2 < H2 / 4) kq[t & 1] = *reinterpret_cast<const f32x4*>(kp + 4 * (t + 2));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = mfma32_f32(kv[e], qf[4 * t + e], s);
+    }
+    // ---- masks: keys past N and, if causal, keys after the query
+    const int key0 = j * BC;
+    bool need = key0 + BC > N;
+    if (CAUSAL) need = need || (key0 + BC - 1 > wq0);
+    if (need) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + acc_row(r, lane);
+        if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+      }
+    }
+    // ---- online softmax: the reference moves only when a lane's sum reaches
+    // kSumBound or the row has none yet (as in the bf16 kernel)
+    float p[16];
+    float rs;
+    auto exps = [&]() {
+      rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = exp2_fast(fmaf(s[r], c, -mu));
+        rs += p[r];
+      }
+    };
+    exps();
+    if (__builtin_amdgcn_ballot_w64(m == -INFINITY || !(rs < kSumBound))) {
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      const float mxr = halves_max(mx) * c;
+      const float m_new = (mxr > m + kLazyRescale) ? mxr : m;
+      const float mu_new = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = m == -INFINITY ? 0.f : exp2_fast(mu - mu_new);  // O and l are 0 while m is -inf
+      m = m_new;
+      mu = mu_new;
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      exps();
+    }
+    l += rs;
+    // ---- O^T += V_j^T P^T
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float* vrow = vs + (8 * (r >> 2) + 4 * half + (r & 3)) * RSF + l32;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b] = mfma32_f32(vrow[32 * b], p[r], o[b]);
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int j = 0; j < nt; ++j) {
+    const int stage = j & 1;
+    if (j + 1 < nt) load_tile(j + 1);
+    if (wave_active && j < nt_w) compute(j, sm[stage], sm[stage] + TILEF);
+    if (j + 1 < nt) store_tile(stage ^ 1);
     __syncthreads();
-    for (int idx = tid; idx < BC * D / 4; idx += 256) {
-      const int row = idx / (D / 4), col = idx % (D / 4);
-      const int key = key0 + row;
-      f32x4 kv = {}, vv = {};
-      if (key < N) {
-        kv = *reinterpret_cast<const f32x4*>(K + head + size_t(key) * D + 4 * col);
-        vv = *reinterpret_cast<const f32x4*>(V + head + size_t(key) * D + 4 * col);
-      }
-      *reinterpret_cast<f32x4*>(Ks + row * D + 4 * col) = kv;
-      *reinterpret_cast<f32x4*>(Vs + row * D + 4 * col) = vv;
-    }
-    __syncthreads();
-    float sc[BC];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kk = 0; kk < BC; ++kk) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(Ks + kk * D + 4 * (i * QL + sub));
-        acc = fmaf(q[i][0], kv[0], acc);
-        acc = fmaf(q[i][1], kv[1], acc);
-        acc = fmaf(q[i][2], kv[2], acc);
-        acc = fmaf(q[i][3], kv[3], acc);
-      }
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      const int key = key0 + kk;
-      float sv = acc * scale;
-      if (key >= N || (CAUSAL && key > qrow)) sv = -INFINITY;
-      sc[kk] = sv;
-      mx = fmaxf(mx, sv);
-    }
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = expf(m - m_use);
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) o[i] *= alpha;
-#pragma unroll
-    for (int kk = 0; kk < BC; ++kk) {
-      const float p = expf(sc[kk] - m_use);
-      l += p;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const f32x4 vv = *reinterpret_cast<const f32x4*>(Vs + kk * D + 4 * (i * QL + sub));
-        o[i][0] = fmaf(p, vv[0], o[i][0]);
-        o[i][1] = fmaf(p, vv[1], o[i][1]);
-        o[i][2] = fmaf(p, vv[2], o[i][2]);
-        o[i][3] = fmaf(p, vv[3], o[i][3]);
-      }
-    }
   }
-  if (qrow >= N) return;
-  const float inv = 1.f / l;
+
+  if (!wave_active) return;
+  const float lt = halves_sum(l);
+  const float inv = 1.f / lt;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head, head_bytes);  // rows past N are dropped by the bounds
 #pragma unroll
-  for (int i = 0; i < NCH; ++i)
-    *reinterpret_cast<f32x4*>(O + head + size_t(qrow) * D + 4 * (i * QL + sub)) = o[i] * inv;
-  if (sub == 0) LSE[size_t(bh) * N + qrow] = m + logf(l);
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(unsigned, o[b][4 * g + e] * inv);
+      __builtin_amdgcn_raw_buffer_store_b128(w, ro, (qrow * D + b * 32 + 8 * g + 4 * half) * 4, 0, 0);
+    }
+  if (half == 0 && qrow < N) LSE[size_t(bh) * N + qrow] = (m + log2_fast(lt)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -890,11 +985,11 @@ hipError_t launch_fwd_blocksparse(const void* q, const void* k, const void* v, v
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_f32_t(const float* q, const float* k, const float* v, float* o, float* lse,
                                    int B, int H, int N, float scale, hipStream_t st) {
-  const int Tr = (N + 63) / 64;
+  const int Tr = (N + 127) / 128;
   const long long G = (long long)B * H * Tr;
   if (G > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)G), dim3(256), 0, st, q, k, v, o, lse, N,
-                     Tr, scale);
+                     Tr, scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -144,7 +144,7 @@ def test_ragged_bf16(gpu_lib, N, d, causal):
     check_lse(f"ragged_bf16 N={N} d={d} causal={causal}", _np(lse), rl)
 
 
-@pytest.mark.parametrize("N", [1, 5, 63, 65, 300])
+@pytest.mark.parametrize("N", [1, 5, 63, 65, 300, 1000, 2049])
 @pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_f32(gpu_lib, N, d, causal):
@@ -154,6 +154,68 @@ def test_ragged_f32(gpu_lib, N, d, causal):
     ro, rl = oracle.ref_fwd(to_f64(q), to_f64(k), to_f64(v), scale, causal)
     check_o(f"ragged_f32 N={N} d={d} causal={causal}", _np(o), ro, fp32=True)
     check_lse(f"ragged_f32 N={N} d={d} causal={causal}", _np(lse), rl, fp32=True)
+
+
+def f32_rounding_bounds(q, k, v, scale, lse_ref):
+    """Worst-case first-order bounds on what an fp32 forward may differ from
+    the exact result when the scores are large (fp64 inputs).  A score
+    sum_i q_i k_i accumulated in fp32 over the d/2 steps of the fp32 MFMA
+    chain (two exact products per step) is off by at most
+    (d/2 + 2) u sum_i |q_i k_i| (u = 2^-24, with the scale multiply and the
+    exponent's FMA), so every weight exp(scale s) is off by a relative
+    eps = scale (d/2 + 2) u max sum|q k|.  A weighted mean of V rows whose
+    weights move by a relative eps moves by at most 2 eps max|v|, and the
+    log of their sum by eps (plus the fp32 rounding of the LSE itself)."""
+    u = 2.0 ** -24
+    d = q.shape[-1]
+    eps = scale * (d / 2 + 2) * u * float(np.einsum("bhid,bhjd->bhij", np.abs(q), np.abs(k)).max())
+    return F32_TOL + 2 * eps * float(np.abs(v).max()), F32_TOL + eps + 4 * u * float(np.abs(lse_ref).max())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_spread_and_far_below_zero(gpu_lib, causal):
+    """The fp32 path on large-spread scores (Q, K ~ N(0, 9): the reference
+    moves on many tiles) and on scores all near -100 (scale 1: about -144 in
+    log2 units, the first reference far below 0), B2 H3 N700 d128.  Scores
+    this large carry fp32 rounding far above 1e-5; both cases are held to the
+    bound of ``f32_rounding_bounds``, derived from it."""
+    q, k, v = make_inputs(2, 3, 700, 128, "f32", seed=260, qk_std=3.0)
+    for tag, scale in (("spread", 128 ** -0.5), ("far below zero", 1.0)):
+        if tag != "spread":
+            q = q * 0.01
+            q[..., 0] = 1.0
+            k = k * 0.01
+            k[..., 0] = -100.0
+        o, lse = _fwd(gpu_lib, q, k, v, causal, scale)
+        qn, kn, vn = to_f64(q), to_f64(k), to_f64(v)
+        ro, rl = oracle.ref_fwd(qn, kn, vn, scale, causal)
+        tol_o, tol_l = f32_rounding_bounds(qn, kn, vn, scale, rl)
+        eo, el = np.abs(_np(o) - ro), np.abs(_np(lse) - rl)
+        name = f"f32 {tag} causal={causal}"
+        _report(check=name, what="O", max_abs=float(eo.max()), mean_abs=float(eo.mean()), bound=tol_o)
+        _report(check=name, what="LSE", max_abs=float(el.max()), bound=tol_l)
+        assert np.isfinite(_np(o)).all() and np.isfinite(_np(lse)).all(), name
+        assert eo.max() <= tol_o, f"{name}: O max-abs {eo.max():.3e} > {tol_o:.3e}"
+        assert el.max() <= tol_l, f"{name}: LSE max-abs {el.max():.3e} > {tol_l:.3e}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_large_sampled_rows(gpu_lib, causal):
+    """The fp32 path on a grid that fills the GPU (B2 H8 N8192 d128, 1024
+    workgroups), sampled rows of every head against the oracle."""
+    B, H, N, d = 2, 8, 8192, 128
+    q, k, v = make_inputs(B, H, N, d, "f32", seed=270)
+    scale = d ** -0.5
+    o, lse = _fwd(gpu_lib, q, k, v, causal, scale)
+    o, lse = _np(o), _np(lse)
+    qn, kn, vn = to_f64(q), to_f64(k), to_f64(v)
+    rng = np.random.default_rng(271)
+    for b in range(B):
+        for h in range(H):
+            rows = sample_rows(N, rng)
+            ro, rl = oracle.ref_fwd_rows(qn[b, h], kn[b, h], vn[b, h], scale, causal, rows)
+            check_o(f"f32 large b={b} h={h} causal={causal}", o[b, h, rows], ro, fp32=True)
+            check_lse(f"f32 large b={b} h={h} causal={causal}", lse[b, h, rows], rl, fp32=True)
 
 
 def test_other_scale_and_peaked_rows(gpu_lib):
