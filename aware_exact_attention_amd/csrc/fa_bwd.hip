@@ -209,26 +209,14 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   const size_t head = size_t(bh) * N * D;
   const int head_bytes = N * T::GRS;
 
-  // K and V fragments of this wave's keys (lane: key k0 + 32*wave + l32,
-  // d = 16*st + 8*half .. +7).  Keys past N read as zero; their dK and dV
-  // rows are never stored.
-  const int key = k0 + wave * 32 + l32;
-  v8 kf[T::KS], vf[T::KS];
-  {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head, head_bytes);
-#pragma unroll
-    for (int st = 0; st < T::KS; ++st) {
-      kf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rk, key * T::GRS + (16 * st + 8 * half) * 2, 0, 0));
-      vf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rv, key * T::GRS + (16 * st + 8 * half) * 2, 0, 0));
-    }
-    // Kept in AGPRs for the whole sweep: the MFMAs take them from there, and
-    // the VGPRs are left to the accumulators and the per-step values.
-#pragma unroll
-    for (int st = 0; st < T::KS; ++st) {
-      asm volatile("" : "+a"(kf[st]));
-      asm volatile("" : "+a"(vf[st]));
-    }
+  const int Tq = (N + T::BQ - 1) / T::BQ;
+  // this workgroup's query steps: [i0, i1), or (block-sparse) the steps
+  // slist[0 .. scount) whose 64-query block keeps one of its two key blocks
+  int i0 = CAUSAL ? k0 / T::BQ : 0, i1 = Tq;
+  if (WINDOW) {
+    // queries i with i - left <= key <= i + right for a key of the workgroup
+    if (mk.right >= 0) i0 = max(0, k0 - mk.right) / T::BQ;
+    if (mk.left >= 0) i1 = (int)min((long long)N - 1, (long long)k0 + T::BKV - 1 + mk.left) / T::BQ + 1;
   }
 
   // Direct-to-LDS loads of the Q and dO tiles of a step: load u of this wave
@@ -254,6 +242,34 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     if (wave == 1) load_lds4(make_rsrc(dh + q0, (N - q0) * 4), smem + stage * T::STAGE + T::OFF_DD, 4 * lane);
   };
 
+  // The first step's Q and dO tiles are requested before the K and V
+  // fragments below, so that the two memory latencies overlap (block-sparse
+  // mode: once its step list is known).
+  const bool early = !BLOCKS && i1 > i0;
+  if (early) issue_loads(i0, 0);
+
+  // K and V fragments of this wave's keys (lane: key k0 + 32*wave + l32,
+  // d = 16*st + 8*half .. +7).  Keys past N read as zero; their dK and dV
+  // rows are never stored.
+  const int key = k0 + wave * 32 + l32;
+  v8 kf[T::KS], vf[T::KS];
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head, head_bytes);
+#pragma unroll
+    for (int st = 0; st < T::KS; ++st) {
+      kf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rk, key * T::GRS + (16 * st + 8 * half) * 2, 0, 0));
+      vf[st] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rv, key * T::GRS + (16 * st + 8 * half) * 2, 0, 0));
+    }
+    // Kept in AGPRs for the whole sweep: the MFMAs take them from there, and
+    // the VGPRs are left to the accumulators and the per-step values.
+#pragma unroll
+    for (int st = 0; st < T::KS; ++st) {
+      asm volatile("" : "+a"(kf[st]));
+      asm volatile("" : "+a"(vf[st]));
+    }
+  }
+
   // Operand offsets: rows l32 (+32 per block) of Q or dO, 16-byte unit
   // 2*st + half; transposing reads as in tr_off.
   int rof[T::KS];
@@ -270,15 +286,6 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
 #pragma unroll
   for (int b = 0; b < T::DBO; ++b) accv[b] = acck[b] = f32x16{};
 
-  const int Tq = (N + T::BQ - 1) / T::BQ;
-  // this workgroup's query steps: [i0, i1), or (block-sparse) the steps
-  // slist[0 .. scount) whose 64-query block keeps one of its two key blocks
-  int i0 = CAUSAL ? k0 / T::BQ : 0, i1 = Tq;
-  if (WINDOW) {
-    // queries i with i - left <= key <= i + right for a key of the workgroup
-    if (mk.right >= 0) i0 = max(0, k0 - mk.right) / T::BQ;
-    if (mk.left >= 0) i1 = (int)min((long long)N - 1, (long long)k0 + T::BKV - 1 + mk.left) / T::BQ + 1;
-  }
   const int kw0 = k0 + wave * 32;  // this wave's first key
   const unsigned char* bm_col = nullptr;  // this wave's key block, row stride nb
   if (BLOCKS) {
@@ -304,7 +311,7 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   auto step_at = [&](int idx) { return BLOCKS ? int(slist[idx]) : i0 + idx; };
 
   if (cnt > 0) {  // uniform over the workgroup; a key block no query sees only stores zeros
-  issue_loads(step_at(0), 0);
+  if (!early) issue_loads(step_at(0), 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
@@ -775,12 +782,31 @@ __global__ void __launch_bounds__(256, 1)
 bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
                 const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
                 E* __restrict__ dK, E* __restrict__ dV, DropArgs dp, int N, int Tk, float c, float scale,
-                MaskArgs mk) {
+                MaskArgs mk, int nblk) {
   __shared__ __attribute__((aligned(1024))) char smem[DkdvTile<D>::LDS];
   __shared__ unsigned short slist[MODE == kMaskBlocks ? kMaxMaskTiles : 1];
   __shared__ int scount;
-  dkdv_block<E, D, CAUSAL, DROP, MODE>(Q, K, V, dO, LSE2, Dv, dK, dV, dp, N, Tk, c, scale, mk, blockIdx.x,
-                                       gridDim.x, smem, slist, scount);
+  // Grids larger than the GPU holds at once (one workgroup per CU) run as
+  // persistent workgroups that take the key blocks in turn.  Block w runs on
+  // a workgroup whose index is w mod 8, so on the XCD a one-block-per-
+  // workgroup launch would give it; round by round the workgroups of an XCD
+  // take its blocks in alternating order, so that longest-first causal
+  // blocks even out over the rounds.  This saves the start of a new
+  // workgroup between blocks (2-4 % at B4 H16 N4096 causal).
+  const int G = gridDim.x;
+  if (G >= nblk) {
+    dkdv_block<E, D, CAUSAL, DROP, MODE>(Q, K, V, dO, LSE2, Dv, dK, dV, dp, N, Tk, c, scale, mk, blockIdx.x,
+                                         nblk, smem, slist, scount);
+    return;
+  }
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3, per = G >> 3;  // G is a multiple of 8
+  for (int i = 0;; ++i) {
+    const int jj = (i & 1) ? per - 1 - j : j;
+    const int w = 8 * (i * per + jj) + x;
+    if (w >= nblk) break;
+    dkdv_block<E, D, CAUSAL, DROP, MODE>(Q, K, V, dO, LSE2, Dv, dK, dV, dp, N, Tk, c, scale, mk, w,
+                                         nblk, smem, slist, scount);
+  }
 }
 
 template <typename E, int D, bool CAUSAL, int NW, bool DROP, int MODE>
@@ -858,9 +884,10 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                        (E*)dq, (E*)dk, (E*)dv, dp, N, Tk, Tr, (int)Gk, c, scale, MaskArgs{});
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, DROP, kMaskDense>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0,
+  const unsigned gk = (unsigned)(Gk > kNumCUs ? kNumCUs : Gk);  // persistent beyond one workgroup per CU
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, DROP, kMaskDense>), dim3(gk), dim3(DkdvTile<D>::NT), 0,
                      st, (const E*)q, (const E*)k, (const E*)v, (const E*)dO,
-                     (const float*)lse2, (const float*)Dv, (E*)dk, (E*)dv, dp, N, Tk, c, scale, MaskArgs{});
+                     (const float*)lse2, (const float*)Dv, (E*)dk, (E*)dv, dp, N, Tk, c, scale, MaskArgs{}, (int)Gk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (D == 128 || D == 96) {
@@ -956,9 +983,10 @@ static hipError_t launch_bwd_masked_t(const void* q, const void* k, const void* 
                        (E*)dq, (E*)dk, (E*)dv, DropArgs{}, N, Tk, Tr, (int)Gk, c, scale, mk);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, false, MODE>), dim3((unsigned)Gk), dim3(DkdvTile<D>::NT), 0, st,
+  const unsigned gk = (unsigned)(Gk > kNumCUs ? kNumCUs : Gk);  // persistent beyond one workgroup per CU
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, false, MODE>), dim3(gk), dim3(DkdvTile<D>::NT), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, (const E*)dO, (const float*)lse2, (const float*)Dv,
-                     (E*)dk, (E*)dv, DropArgs{}, N, Tk, c, scale, mk);
+                     (E*)dk, (E*)dv, DropArgs{}, N, Tk, c, scale, mk, (int)Gk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<E, D, CAUSAL, 4, false, MODE>), dim3((unsigned)Gq), dim3(DqTile<D, 4>::NT), 0, st,
