@@ -128,7 +128,8 @@ bwd_pre_kernel(const E* __restrict__ O, const E* __restrict__ dO, const float* _
 // and the VALU work is spread over the slots whose MFMAs do not depend on
 // it, two elements per slot: P of the first 32-query block while its dP
 // MFMAs run, its dS during the S MFMAs of the second block, and so on.
-// Each slot also issues the LDS read of the operand three slots ahead.
+// Each slot also issues the LDS read of the operand three slots ahead, and
+// every second one of the first slots one direct load of the next step.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvTile {
@@ -318,7 +319,27 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   for (int idx = 0; idx < cnt; ++idx) {
     const int i = step_at(idx);
     const int stage = idx & 1;
-    if (idx + 1 < cnt) issue_loads(step_at(idx + 1), stage ^ 1);
+    // The next step's tiles are requested one load every second slot of the
+    // schedule below, among the first MFMAs: the whole batch at the top of
+    // the step held the wave (the only one on its SIMD) at the vector memory
+    // unit.  On the last step the resources have size 0 and the loads read
+    // nothing.
+    const bool has_next = idx + 1 < cnt;
+    const int qn = has_next ? step_at(idx + 1) * T::BQ : 0;
+    const int nbytes = has_next ? (N - qn) * T::GRS : 0;
+    const __amdgpu_buffer_rsrc_t nrq = make_rsrc(Q + head + size_t(qn) * D, nbytes);
+    const __amdgpu_buffer_rsrc_t nrd = make_rsrc(dO + head + size_t(qn) * D, nbytes);
+    const __amdgpu_buffer_rsrc_t nrs =
+        make_rsrc((wave == 0 ? lse2h : dh) + qn, has_next ? (N - qn) * 4 : 0);
+    char* ndst = smem + (stage ^ 1) * T::STAGE;
+    constexpr int NL = 2 * T::LPW + 1;
+    auto issue_one = [&](auto lc) {
+      constexpr int l = decltype(lc)::value;
+      if constexpr (l < T::LPW) load_lds16(nrq, ndst + wave * T::LPW * 1024 + l * 1024, goff[l]);
+      else if constexpr (l < 2 * T::LPW)
+        load_lds16(nrd, ndst + T::OFF_DO + wave * T::LPW * 1024 + (l - T::LPW) * 1024, goff[l - T::LPW]);
+      else if (wave < 2) load_lds4(nrs, ndst + (wave == 0 ? T::OFF_LSE : T::OFF_DD), 4 * lane);
+    };
     const char* sb = smem + stage * T::STAGE;
     const int qs = i * T::BQ;
     // steps whose element mask matters for this wave's keys: causal, the two
@@ -414,6 +435,7 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
         if constexpr (!is_dk) accv[b] = mfma32(a, op[ps], accv[b]);
         else acck[b] = mfma32(a, os[ps], acck[b]);
       }
+      if constexpr (u % 2 == 0 && u / 2 < NL) issue_one(std::integral_constant<int, u / 2>{});
       if constexpr (u + PF < T::SLOTS) ring[u % PF] = fetch(std::integral_constant<int, u + PF>{});
       // masks: S = -inf (P = 0) where the key is after the query (causal),
       // outside the query's window, or in a dropped block, on the steps that

@@ -213,9 +213,9 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   int goff[T::LPW];
 #pragma unroll
   for (int i = 0; i < T::LPW; ++i) goff[i] = swz_src<D>((rg * T::LPW + i) * 1024 + 16 * lane);
-  auto issue_loads = [&](int j, int stage) {
-    const int key0 = j * T::BC;
-    const int bytes = (N - key0) * T::GRS;
+  auto issue_loads = [&](int j, int stage, bool valid = true) {
+    const int key0 = valid ? j * T::BC : 0;
+    const int bytes = valid ? (N - key0) * T::GRS : 0;  // not valid: the loads read nothing
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + size_t(key0) * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + size_t(key0) * D, bytes);
     char* kdst = (stage ? smem1 : smem0) + kp * T::STAGE + rg * T::LPW * 1024;
@@ -254,7 +254,7 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   float mu = 0.f;       // m, or 0 while m is -inf: the value subtracted before exp2
   float l = 0.f;        // running sum over this lane's half of the keys
 
-  auto compute = [&](int j, const char* base) {
+  auto compute = [&](int j, const char* base, int nj, bool has_next, int nstage) {
     // ---- S^T = K_j Q^T: one independent chain per 32-key block; K operands are read
     // KPF k steps ahead, an order pinned by scheduling barriers (left alone,
     // the scheduler pulls each read next to its MFMA and the LDS latency shows)
@@ -276,11 +276,16 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
         for (int kb = 0; kb < T::KB; ++kb)
           kr[st % KPF][kb] = *reinterpret_cast<const v8*>(base + kof[st + KPF] + kb * 32 * T::RS);
     }
+    // the next tile's direct loads go out one after each of the first MFMA
+    // groups: issued in one burst at the top of the step, they held the wave
+    // at the vector memory unit while its matrix unit had nothing to do
+    issue_loads(nj, nstage, has_next);
     __builtin_amdgcn_sched_group_barrier(0x100, T::KB * KPF, 0);
 #pragma unroll
     for (int st = 0; st < T::KS; ++st) {
       __builtin_amdgcn_sched_group_barrier(0x008, T::KB, 0);
       if (st + KPF < T::KS) __builtin_amdgcn_sched_group_barrier(0x100, T::KB, 0);
+      if (st < 2 * T::LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     // ---- masks: keys past N and, if causal, keys after the query; for a
     // window, keys outside [qrow - left, qrow + right].  Only tiles that cross
@@ -387,12 +392,20 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   };
 
   // step idx: tile tile_at(idx) from stage `stage`, loads of the next tile into the other
+  // (inside compute when the wave computes this tile; after the last tile the
+  // loads have size 0 and read nothing)
   auto step = [&](int idx, int stage) {
-    if (idx + 1 < cnt_w) issue_loads(tile_at(idx + 1), stage ^ 1);
+    const bool has_next = idx + 1 < cnt_w;
+    const int nj = has_next ? tile_at(idx + 1) : 0;
+    bool issued = false;
     if (idx < cnt_w) {
       const int j = tile_at(idx);
-      if (wave_needs(j)) compute(j, (stage ? smem1 : smem0) + kp * T::STAGE);
+      if (wave_needs(j)) {
+        compute(j, (stage ? smem1 : smem0) + kp * T::STAGE, nj, has_next, stage ^ 1);
+        issued = true;
+      }
     }
+    if (!issued && has_next) issue_loads(nj, stage ^ 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the next tile have landed
     __syncthreads();
   };
