@@ -69,20 +69,21 @@ def test_dropout_backward(gpu_lib, N, d, causal, p):
 
 def test_dropout_larger(gpu_lib):
     """B1 H2 N4096 d128 (four-wave forward) and B1 H64 N2048 d128 (eight-wave
-    forward and dQ kernels) at p = 0.1, compared on the last head."""
-    for (B, H, N) in ((1, 2, 4096), (1, 64, 2048)):
+    forward and dQ kernels, persistent dK/dV workgroups), dense and causal, at
+    p = 0.1, compared on the last head."""
+    for (B, H, N, causal) in ((1, 2, 4096, False), (1, 64, 2048, False), (1, 64, 2048, True)):
         q, k, v, do = make_inputs(B, H, N, 128, "bf16", seed=1500 + H, backward=True)
         scale, seed, p = 128 ** -0.5, 4242, 0.1
         qd, kd, vd, dod = _gpu(q, k, v, do)
-        o, lse = gpu_lib.fwd_dropout(qd, kd, vd, p, seed, scale=scale)
-        dq, dk, dv = gpu_lib.bwd_dropout(qd, kd, vd, o, lse, dod, p, seed, scale=scale)
+        o, lse = gpu_lib.fwd_dropout(qd, kd, vd, p, seed, causal=causal, scale=scale)
+        dq, dk, dv = gpu_lib.bwd_dropout(qd, kd, vd, o, lse, dod, p, seed, causal=causal, scale=scale)
         torch.cuda.synchronize()
         h = H - 1
         sl = (slice(0, 1), slice(h, h + 1))
         args = [to_f64(t[sl]) for t in (q, k, v, do)]
-        ro, rl = oracle.ref_fwd_dropout(*args[:3], scale, False, p, seed, bh0=h)
-        rq, rk, rv = oracle.ref_bwd_dropout(*args, scale, False, p, seed, bh0=h)
-        tag = f"dropout B{B} H{H} N{N} head {h}"
+        ro, rl = oracle.ref_fwd_dropout(*args[:3], scale, causal, p, seed, bh0=h)
+        rq, rk, rv = oracle.ref_bwd_dropout(*args, scale, causal, p, seed, bh0=h)
+        tag = f"dropout B{B} H{H} N{N} causal={causal} head {h}"
         check_o(tag, _np(o)[sl], ro)
         check_lse(tag, _np(lse)[sl], rl)
         check_grad(tag, "dQ", _np(dq)[sl], rq)

@@ -114,6 +114,19 @@ def test_masks_bwd_each_launch_shape(gpu_lib, H, N, d):
     _check_blocks(f"bwd blocksparse launch shape H={H} N={N} d={d}", got, ref, bm, True, N)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_bwd_persistent(gpu_lib, d):
+    """Window (40, 70) over B2 H96 N300: 576 key blocks, so the dK/dV pass runs
+    as persistent workgroups that bring each block's K, V and first tiles in
+    during the previous block; the blocks' query-step ranges differ at both
+    ends.  Compared in full."""
+    q, k, v, do = make_inputs(2, 96, 300, d, "bf16", seed=1760 + d, backward=True)
+    scale = d ** -0.5
+    got = _window_case(gpu_lib, q, k, v, do, 40, 70, scale)
+    _check3(f"bwd window persistent d={d}", got, oracle.ref_bwd_window(*(to_f64(t) for t in (q, k, v, do)),
+                                                                       scale, 40, 70))
+
+
 def test_blocksparse_bwd_all_ones_equals_dense(gpu_lib):
     """An all-ones mask visits the same steps and tiles in the same order as
     the dense backward, so the gradients agree bit for bit."""

@@ -497,6 +497,25 @@ def test_bwd_ragged_many_heads(gpu_lib, d, causal):
     check_grad(tag, "dV", dv, rv)
 
 
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_persistent_key_blocks(gpu_lib, d, causal):
+    """More 128-key blocks than CUs (B2 H96 N300: 576 blocks) run the dK/dV
+    pass as persistent workgroups, where each block's K, V and first Q/dO
+    tiles come into LDS during the workgroup's previous block.  N = 300 gives
+    every head a last block whose second 64-key half lies wholly past N, and
+    (causal) blocks of a single query step, whose first step is also the one
+    that brings in the next block.  Compared in full."""
+    q, k, v, do = make_inputs(2, 96, 300, d, "bf16", seed=470 + d, backward=True)
+    scale = d ** -0.5
+    _, _, dq, dk, dv = _bwd_case(gpu_lib, q, k, v, do, causal, scale)
+    rq, rk, rv = oracle.ref_bwd(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal)
+    tag = f"bwd persistent B2 H96 N=300 d={d} causal={causal}"
+    check_grad(tag, "dQ", dq, rq)
+    check_grad(tag, "dK", dk, rk)
+    check_grad(tag, "dV", dv, rv)
+
+
 _FULL_BWD_CASES = [("fwd_bwd_causal", b) for b in range(4)] + [("bwd_16k", (0, 4)), ("bwd_16k", (4, 8))]
 
 
