@@ -191,8 +191,10 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
            char* kvs = nullptr, int stage0 = 0, bool pre = false, int nextw = -1) {
   using T = DkdvTile<D>;
   using v8 = typename Vec<E>::v8;
-  constexpr int M = T::M, H = T::H, PF = T::PF;
   constexpr bool WINDOW = MODE == kMaskWindow, BLOCKS = MODE == kMaskBlocks;
+  // block-sparse: two operand reads in flight, not three (with three, the
+  // kernel that runs both passes in one grid spilled an operand at d = 128)
+  constexpr int M = T::M, H = T::H, PF = BLOCKS ? 2 : T::PF;
   static_assert(!(DROP && MODE != kMaskDense), "dropout only with the dense or causal mask");
   static_assert(!BLOCKS || (T::BQ == kMaskBlock && T::BKV == 2 * kMaskBlock), "query steps are mask blocks");
   static_assert(!STAGED || (T::OS == 1 && !BLOCKS && 8 * T::LPW <= T::SLOTS),
@@ -343,20 +345,22 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   for (int b = 0; b < T::DBO; ++b) accv[b] = acck[b] = f32x16{};
 
   const int kw0 = k0 + wave * 32;  // this wave's first key
-  const unsigned char* bm_col = nullptr;  // this wave's key block, row stride nb
+  // block-sparse: each step of the list carries the keep flags of the
+  // workgroup's two 64-key blocks (waves 0-1 and 2-3)
   if (BLOCKS) {
     const unsigned char* bmh = mk.bm + mk.bm_head_stride * (bh % mk.H);
     const int kb0 = k0 / kMaskBlock;
     const bool two = kb0 + 1 < mk.nb;
-    bm_col = bmh + min(kw0, N - 1) / kMaskBlock;
     if (wave == 0) {
       int n = 0;
       for (int base = i0; base < Tq; base += 64) {
         const int ii = base + lane;
-        const bool keep = ii < Tq && (bmh[size_t(ii) * mk.nb + kb0] != 0 || (two && bmh[size_t(ii) * mk.nb + kb0 + 1] != 0));
+        const bool a0 = ii < Tq && bmh[size_t(ii) * mk.nb + kb0] != 0;
+        const bool a1 = ii < Tq && two && bmh[size_t(ii) * mk.nb + kb0 + 1] != 0;
+        const bool keep = a0 || a1;
         const unsigned long long bal = __builtin_amdgcn_ballot_w64(keep);
         const int below = __builtin_popcountll(bal & ((1ull << lane) - 1));
-        if (keep) slist[n + below] = (unsigned short)ii;
+        if (keep) slist[n + below] = list_entry(ii, a0, a1);
         n += __builtin_popcountll(bal);
       }
       if (lane == 0) scount = n;
@@ -364,7 +368,7 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     __syncthreads();
   }
   const int cnt = BLOCKS ? scount : i1 - i0;
-  auto step_at = [&](int idx) { return BLOCKS ? int(slist[idx]) : i0 + idx; };
+  auto step_at = [&](int idx) { return BLOCKS ? list_index(slist[idx]) : i0 + idx; };
 
   // the next key block of a persistent workgroup, staged by the last step
   // when it has query steps
@@ -416,6 +420,10 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
         load_lds16(nrd, ndst + T::OFF_DO + wave * T::LPW * 1024 + (l - T::LPW) * 1024, goff[l - T::LPW]);
       else if (wave < 2) load_lds4(nrs, ndst + (wave == 0 ? T::OFF_LSE : T::OFF_DD), 4 * lane);
     };
+    // block-sparse: all at once here (spread over the slots, the step-list
+    // bookkeeping pushed the kernel past its registers)
+    if constexpr (BLOCKS)
+      if (has_next) static_for<NL>([&](auto lc) { issue_one(lc); });
     const char* sb = smem + stage * T::STAGE;
     const int qs = i * T::BQ;
     // steps whose element mask matters for this wave's keys: causal, the two
@@ -424,7 +432,7 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     bool need = CAUSAL && kw0 + 31 > qs;
     if (WINDOW)
       need = need || (mk.left >= 0 && kw0 < qs + T::BQ - 1 - mk.left) || (mk.right >= 0 && kw0 + 31 > qs + mk.right);
-    const bool dead = BLOCKS && bm_col[size_t(i) * mk.nb] == 0;
+    const bool dead = BLOCKS && !list_keeps(slist[idx], wave >> 1);
     if (BLOCKS) need = need || dead;
 
     f32x16 s[T::QB], pd[T::QB];  // S and dP; lane: key, element j: query 32*qb + acc_row(j)
@@ -511,7 +519,7 @@ dkdv_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
         if constexpr (!is_dk) accv[b] = mfma32(a, op[ps], accv[b]);
         else acck[b] = mfma32(a, os[ps], acck[b]);
       }
-      if constexpr (u % 2 == 0 && u / 2 < NL) issue_one(std::integral_constant<int, u / 2>{});
+      if constexpr (!BLOCKS && u % 2 == 0 && u / 2 < NL) issue_one(std::integral_constant<int, u / 2>{});
       if constexpr (LAST && u % 2 == 1 && u / 2 < 4 * T::LPW)
         if (has_next) kv_load(nkv, u / 2);
       if constexpr (u + PF < T::SLOTS) ring[u % PF] = fetch(std::integral_constant<int, u + PF>{});
@@ -683,20 +691,22 @@ dq_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__
     w0 = mk.left >= 0 ? max(0, wq0 - mk.left) / T::BC : 0;
     nt_w = mk.right >= 0 ? (int)((min((long long)N, (long long)wq0 + 32 + mk.right) - 1) / T::BC + 1) : Tc;
   }
-  const unsigned char* bm_row = nullptr;
+  // block-sparse: each tile of the list carries the keep flags of the
+  // workgroup's two 64-row blocks (waves 0-1 and 2-3)
   if (BLOCKS) {
     const unsigned char* bmh = mk.bm + mk.bm_head_stride * (bh % mk.H);
-    bm_row = bmh + size_t(min(wq0, N - 1) / kMaskBlock) * mk.nb;
     if (wave == 0) {
       const unsigned char* r0 = bmh + size_t(q0 / kMaskBlock) * mk.nb;
       const bool two = q0 + kMaskBlock < N;
       int n = 0;
       for (int base = 0; base < nt; base += 64) {
         const int jj = base + lane;
-        const bool keep = jj < nt && (r0[jj] != 0 || (two && r0[mk.nb + jj] != 0));
+        const bool a0 = jj < nt && r0[jj] != 0;
+        const bool a1 = jj < nt && two && r0[mk.nb + jj] != 0;
+        const bool keep = a0 || a1;
         const unsigned long long bal = __builtin_amdgcn_ballot_w64(keep);
         const int below = __builtin_popcountll(bal & ((1ull << lane) - 1));
-        if (keep) tlist[n + below] = (unsigned short)jj;
+        if (keep) tlist[n + below] = list_entry(jj, a0, a1);
         n += __builtin_popcountll(bal);
       }
       if (lane == 0) tcount = n;
@@ -704,10 +714,10 @@ dq_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__
     __syncthreads();
   }
   const int cnt = BLOCKS ? tcount : nt - j0;
-  auto tile_at = [&](int idx) { return BLOCKS ? int(tlist[idx]) : j0 + idx; };
-  auto wave_needs = [&](int j) {
+  auto tile_at = [&](int idx) { return BLOCKS ? list_index(tlist[idx]) : j0 + idx; };
+  auto wave_needs = [&](int idx, int j) {
     if (!wave_active || j >= nt_w || j < w0) return false;
-    return !BLOCKS || bm_row[j] != 0;
+    return !BLOCKS || list_keeps(tlist[idx], wave >> 1);
   };
 
   int goff[T::LPW];
@@ -851,7 +861,7 @@ dq_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__
   auto step = [&](int idx, int stage) {
     if (idx + 1 < cnt) issue_loads(tile_at(idx + 1), stage ^ 1);
     const int j = tile_at(idx);
-    if (wave_needs(j)) compute(j, smem + stage * T::STAGE);
+    if (wave_needs(idx, j)) compute(j, smem + stage * T::STAGE);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the next tile have landed
     __syncthreads();
   };
@@ -885,20 +895,29 @@ dq_block(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__
 // ---------------------------------------------------------------------------
 // kernels
 // ---------------------------------------------------------------------------
+// LDS bytes after a kernel's stages for a block-sparse step or tile list
+// (kMaxMaskTiles entries) and its count; other modes keep 16 unused bytes.
+constexpr int list_bytes(int mode) { return mode == kMaskBlocks ? 2 * kMaxMaskTiles + 16 : 16; }
+__device__ __forceinline__ int& list_count(unsigned short* list, int mode) {
+  return *reinterpret_cast<int*>(reinterpret_cast<char*>(list) + (mode == kMaskBlocks ? 2 * kMaxMaskTiles : 0));
+}
+
 template <typename E, int D, bool CAUSAL, bool DROP, int MODE>
 __global__ void __launch_bounds__(256, 1)
 bwd_dkdv_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
                 const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
                 E* __restrict__ dK, E* __restrict__ dV, DropArgs dp, int N, int Tk, float c, float scale,
                 MaskArgs mk, int nblk) {
-  // staged K and V rows (persistent workgroups) after the two stages, in the
-  // same array: the compiler then keeps the stage reads free of waits for
-  // the direct loads
+  // One LDS array holds the two stages, the staged K and V rows (persistent
+  // workgroups) and the step list with its count (block-sparse): with a
+  // second __shared__ variable in the kernel, hipcc waits for every direct
+  // load before the next LDS read.
   constexpr bool kStaged = D <= 128 && MODE != kMaskBlocks;
-  __shared__ __attribute__((aligned(1024))) char smem[DkdvTile<D>::LDS + (kStaged ? DkdvTile<D>::KVS : 0)];
-  __shared__ unsigned short slist[MODE == kMaskBlocks ? kMaxMaskTiles : 1];
-  __shared__ int scount;
+  constexpr int kKvs = kStaged ? DkdvTile<D>::KVS : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[DkdvTile<D>::LDS + kKvs + list_bytes(MODE)];
   char* const kvs = smem + DkdvTile<D>::LDS;
+  unsigned short* const slist = reinterpret_cast<unsigned short*>(smem + DkdvTile<D>::LDS + kKvs);
+  int& scount = list_count(slist, MODE);
   // Grids larger than the GPU holds at once (one workgroup per CU) run as
   // persistent workgroups that take the key blocks in turn.  Block w runs on
   // a workgroup whose index is w mod 8, so on the XCD a one-block-per-
@@ -934,9 +953,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
 bwd_dq_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
               const E* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dv,
               E* __restrict__ dQ, DropArgs dp, int N, int Tr, float c, float scale, MaskArgs mk) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * DqTile<D, NW>::STAGE];
-  __shared__ unsigned short tlist[MODE == kMaskBlocks ? kMaxMaskTiles : 1];
-  __shared__ int tcount;
+  // the tile list and its count (block-sparse) in the stages' array, as in the dK/dV pass
+  __shared__ __attribute__((aligned(1024))) char smem[2 * DqTile<D, NW>::STAGE + list_bytes(MODE)];
+  unsigned short* const tlist = reinterpret_cast<unsigned short*>(smem + 2 * DqTile<D, NW>::STAGE);
+  int& tcount = list_count(tlist, MODE);
   dq_block<E, D, CAUSAL, NW, DROP, MODE>(Q, K, V, dO, LSE2, Dv, dQ, dp, N, Tr, c, scale, mk, blockIdx.x, gridDim.x,
                                          smem, tlist, tcount);
 }
@@ -953,9 +973,9 @@ bwd_both_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __res
                 E* __restrict__ dQ, E* __restrict__ dK, E* __restrict__ dV, DropArgs dp, int N, int Tk, int Tr,
                 int Gk, float c, float scale, MaskArgs mk) {
   constexpr int kLds = DkdvTile<D>::LDS > 2 * DqTile<D, 4>::STAGE ? DkdvTile<D>::LDS : 2 * DqTile<D, 4>::STAGE;
-  __shared__ __attribute__((aligned(1024))) char smem[kLds];
-  __shared__ unsigned short list[MODE == kMaskBlocks ? kMaxMaskTiles : 1];
-  __shared__ int count;
+  __shared__ __attribute__((aligned(1024))) char smem[kLds + list_bytes(MODE)];
+  unsigned short* const list = reinterpret_cast<unsigned short*>(smem + kLds);
+  int& count = list_count(list, MODE);
   const int bid = blockIdx.x;
   if (bid < Gk)
     dkdv_block<E, D, CAUSAL, DROP, MODE>(Q, K, V, dO, LSE2, Dv, dK, dV, dp, N, Tk, c, scale, mk, bid, Gk, smem, list,

@@ -289,6 +289,18 @@ __device__ __forceinline__ unsigned quad_share_nibbles(unsigned mine, unsigned t
 enum : int { kMaskDense = 0, kMaskWindow = 1, kMaskBlocks = 2 };
 constexpr int kMaskBlock = 64;
 constexpr int kMaxMaskTiles = 1024;  // block-sparse: N <= 65536
+
+// Entries of a workgroup's block-sparse tile (or step) list: the index in
+// bits 0-13 and, in bits 14 and 15, whether the mask keeps that tile for the
+// workgroup's first and second 64-row (or 64-key) block.  A wave then learns
+// whether its own block keeps a tile from the list in LDS, with no load from
+// the mask inside the sweep.
+static_assert(kMaxMaskTiles <= (1 << 14), "list indices fit in 14 bits");
+__device__ __forceinline__ unsigned short list_entry(int index, bool first, bool second) {
+  return (unsigned short)(index | (int(first) << 14) | (int(second) << 15));
+}
+__device__ __forceinline__ int list_index(unsigned short e) { return e & 0x3FFF; }
+__device__ __forceinline__ bool list_keeps(unsigned short e, int block) { return (e >> (14 + block)) & 1; }
 struct MaskArgs {
   int left, right;
   const unsigned char* bm;

@@ -168,23 +168,24 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     w0 = mk.left >= 0 ? max(0, wq0 - mk.left) / T::BC : 0;
     nt_w = mk.right >= 0 ? (min(N, wq0 + 32 + mk.right) - 1) / T::BC + 1 : Tc;
   }
-  // block-sparse: the workgroup's tiles, in order, in tlist[0 .. tcount); a
-  // wave computes a tile only if its own 64-row block keeps it
-  const unsigned char* bm_row = nullptr;
+  // block-sparse: the workgroup's tiles, in order, in tlist[0 .. tcount),
+  // each with the keep flags of the workgroup's two 64-row blocks; a wave
+  // (rows of block wave / 2) computes a tile only if its own block keeps it
   if (BLOCKS) {
     const int h = bh % mk.H;
     const unsigned char* bmh = mk.bm + mk.bm_head_stride * h;
-    bm_row = bmh + size_t(min(wq0, N - 1) / kMaskBlock) * mk.nb;
     if (wave == 0) {
       const unsigned char* r0 = bmh + size_t(q0 / kMaskBlock) * mk.nb;
       const bool two = q0 + kMaskBlock < N;  // the workgroup's second 64-row block exists
       int n = 0;
       for (int base = 0; base < nt; base += 64) {
         const int jj = base + lane;
-        const bool keep = jj < nt && (r0[jj] != 0 || (two && r0[mk.nb + jj] != 0));
+        const bool a0 = jj < nt && r0[jj] != 0;
+        const bool a1 = jj < nt && two && r0[mk.nb + jj] != 0;
+        const bool keep = a0 || a1;
         const unsigned long long bal = __builtin_amdgcn_ballot_w64(keep);
         const int below = __builtin_popcountll(bal & ((1ull << lane) - 1));
-        if (keep) tlist[n + below] = (unsigned short)jj;
+        if (keep) tlist[n + below] = list_entry(jj, a0, a1);
         n += __builtin_popcountll(bal);
       }
       if (lane == 0) tcount = n;
@@ -201,10 +202,10 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
   }
   const int cnt = BLOCKS ? tcount : tpk;                  // steps of the workgroup
   const int cnt_w = BLOCKS ? cnt : max(0, pj1 - pj0);     // steps with a tile of this wave's part
-  auto tile_at = [&](int idx) { return BLOCKS ? int(tlist[idx]) : pj0 + idx; };
-  auto wave_needs = [&](int j) {
+  auto tile_at = [&](int idx) { return BLOCKS ? list_index(tlist[idx]) : pj0 + idx; };
+  auto wave_needs = [&](int idx, int j) {
     if (!wave_active || j >= nt_w || j < w0) return false;
-    return !BLOCKS || bm_row[j] != 0;
+    return !BLOCKS || list_keeps(tlist[idx], wave >> 1);
   };
 
   // Direct-to-LDS tile loads: load i of this wave fills LDS bytes
@@ -400,7 +401,7 @@ fwd_kernel(const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict
     bool issued = false;
     if (idx < cnt_w) {
       const int j = tile_at(idx);
-      if (wave_needs(j)) {
+      if (wave_needs(idx, j)) {
         compute(j, (stage ? smem1 : smem0) + kp * T::STAGE, nj, has_next, stage ^ 1);
         issued = true;
       }
